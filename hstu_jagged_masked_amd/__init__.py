@@ -1,0 +1,212 @@
+"""HSTU jagged masked attention on MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libhstu_attn.so`` (built in-tree by
+``hstu_jagged_masked_amd.build``).  It only marshals arguments: every step of
+the operator runs in the library's HIP kernels.  PyTorch provides device
+memory and the current stream.  There is no CPU or PyTorch fallback: if the
+library is missing the import of the op raises.
+
+Entry points mirror the C ABI (include/hstu_attn.h):
+
+    attn_fwd(q, k, v, seq_offsets, func, alpha, max_len, target_rows=None) -> o
+    attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None) -> dq, dk, dv
+    visible_counts(seq_offsets, func, total, target_rows=None) -> (counts, total_pairs)
+    check_inputs(seq_offsets, total, target_rows=None)
+    hstu_attention(...)  # autograd.Function wrapper of the two above
+
+Tensors: q, k, v, dout are CUDA tensors ``[rows, H, D]`` (bfloat16 or float32,
+contiguous); in targets-only mode q and dout are ``[B, H, D]``.  ``seq_offsets``
+is int64 ``[B+1]``, ``func`` int32 ``[nfunc, total]``, ``target_rows`` int32
+``[B]``, all on the same device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libhstu_attn.so")
+
+HSTU_BF16 = 0
+HSTU_FP32 = 1
+_STATUS = {0: "OK", -1: "invalid argument", -2: "unsupported", -3: "workspace too small",
+           -4: "device error", -5: "malformed input"}
+
+_lib = None
+
+
+class HstuError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"hstu_attn: {_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Load libhstu_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is missing: build it with "
+                          "`python -m hstu_jagged_masked_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIBRARY)
+    P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    lib.hstu_max_nfunc.argtypes = []
+    lib.hstu_max_nfunc.restype = i32
+    lib.hstu_last_error.argtypes = []
+    lib.hstu_last_error.restype = ctypes.c_char_p
+    lib.hstu_attn_workspace_size.argtypes = [i32, i32, i64, i64, i32, i32, i32, i32]
+    lib.hstu_attn_workspace_size.restype = sz
+    lib.hstu_attn_fwd.argtypes = [i32, P, P, P, P, P, i64, i64, i32, i32, P, i32, f32, i64, P, P,
+                                  sz, P]
+    lib.hstu_attn_fwd.restype = i32
+    lib.hstu_attn_bwd.argtypes = [i32, P, P, P, P, P, P, P, P, i64, i64, i32, i32, P, i32, f32,
+                                  i64, P, P, sz, P]
+    lib.hstu_attn_bwd.restype = i32
+    lib.hstu_attn_visible_counts.argtypes = [P, i64, i64, P, i32, P, P, P, P]
+    lib.hstu_attn_visible_counts.restype = i32
+    lib.hstu_attn_check_inputs.argtypes = [P, i64, i64, P, P, sz, P]
+    lib.hstu_attn_check_inputs.restype = i32
+    _lib = lib
+    return lib
+
+
+EXPORTED = ("hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size", "hstu_attn_fwd",
+            "hstu_attn_bwd", "hstu_attn_visible_counts", "hstu_attn_check_inputs")
+
+
+def _check(status: int):
+    if status != 0:
+        msg = library().hstu_last_error()
+        raise HstuError(status, msg.decode() if msg else "")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HSTU_BF16
+    if t.dtype == torch.float32:
+        return HSTU_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def max_nfunc() -> int:
+    return library().hstu_max_nfunc()
+
+
+def workspace_size(is_bwd, dtype_code, B, total, H, D, nfunc, targets_only) -> int:
+    return int(library().hstu_attn_workspace_size(int(is_bwd), int(dtype_code), int(B), int(total),
+                                                  int(H), int(D), int(nfunc), int(targets_only)))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _common(q, k, seq_offsets, func, target_rows):
+    if k.dim() != 3:
+        raise ValueError("k must be [total, H, D]")
+    total, H, D = k.shape
+    B = seq_offsets.numel() - 1
+    if func.dim() != 2 or func.shape[1] != total:
+        raise ValueError("func must be [nfunc, total] int32")
+    if seq_offsets.dtype != torch.int64 or func.dtype != torch.int32:
+        raise TypeError("seq_offsets must be int64 and func int32")
+    if target_rows is not None:
+        if target_rows.dtype != torch.int32 or target_rows.numel() != B:
+            raise ValueError("target_rows must be int32 [B]")
+        if q.shape[0] != B:
+            raise ValueError("in targets-only mode q must be [B, H, D]")
+    elif q.shape[0] != total:
+        raise ValueError("q must be [total, H, D]")
+    for t in (seq_offsets, func, target_rows):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("seq_offsets, func and target_rows must be contiguous")
+    return B, total, H, D, func.shape[0]
+
+
+def attn_fwd(q, k, v, seq_offsets, func, alpha, max_len, target_rows=None, out=None):
+    B, total, H, D, nfunc = _common(q, k, seq_offsets, func, target_rows)
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype != k.dtype:
+            raise ValueError("q, k, v must be contiguous and share a dtype")
+    code = _dtype_code(k)
+    o = torch.empty_like(q) if out is None else out
+    ws_bytes = workspace_size(0, code, B, total, H, D, nfunc, target_rows is not None)
+    ws = _workspace(ws_bytes, k.device)
+    _check(library().hstu_attn_fwd(
+        code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_offsets), B, total, H, D, _ptr(func),
+        nfunc, float(alpha), int(max_len), _ptr(target_rows), _ptr(ws), ws.numel(),
+        _stream(k.device)))
+    return o
+
+
+def attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None):
+    B, total, H, D, nfunc = _common(q, k, seq_offsets, func, target_rows)
+    for t in (q, k, v, dout):
+        if not t.is_contiguous() or t.dtype != k.dtype:
+            raise ValueError("q, k, v, dout must be contiguous and share a dtype")
+    code = _dtype_code(k)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws_bytes = workspace_size(1, code, B, total, H, D, nfunc, target_rows is not None)
+    ws = _workspace(ws_bytes, k.device)
+    _check(library().hstu_attn_bwd(
+        code, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(seq_offsets), B, total, H, D, _ptr(func), nfunc, float(alpha), int(max_len),
+        _ptr(target_rows), _ptr(ws), ws.numel(), _stream(k.device)))
+    return dq, dk, dv
+
+
+def visible_counts(seq_offsets, func, total=None, target_rows=None):
+    """Per-row visible-column counts (int32) and their sum (int64 tensor)."""
+    B = seq_offsets.numel() - 1
+    total = func.shape[1] if total is None else int(total)
+    n = B if target_rows is not None else total
+    counts = torch.empty(n, dtype=torch.int32, device=func.device)
+    tot = torch.empty(1, dtype=torch.int64, device=func.device)
+    _check(library().hstu_attn_visible_counts(
+        _ptr(seq_offsets), B, total, _ptr(func), func.shape[0], _ptr(target_rows), _ptr(counts),
+        _ptr(tot), _stream(func.device)))
+    return counts, tot
+
+
+def check_inputs(seq_offsets, total, target_rows=None):
+    """Validate device-resident offsets / target rows (synchronizes)."""
+    B = seq_offsets.numel() - 1
+    ws = _workspace(workspace_size(0, HSTU_BF16, B, total, 1, 128, 1, 0), seq_offsets.device)
+    _check(library().hstu_attn_check_inputs(_ptr(seq_offsets), B, int(total), _ptr(target_rows),
+                                            _ptr(ws), ws.numel(), _stream(seq_offsets.device)))
+
+
+class HstuAttention(torch.autograd.Function):
+    """Autograd wrapper: forward = attn_fwd, backward = attn_bwd (nothing saved
+    but the inputs: HSTU attention has no softmax statistics to keep)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, seq_offsets, func, alpha, max_len, target_rows):
+        ctx.save_for_backward(q, k, v, seq_offsets, func, target_rows)
+        ctx.alpha, ctx.max_len = alpha, max_len
+        return attn_fwd(q, k, v, seq_offsets, func, alpha, max_len, target_rows)
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, seq_offsets, func, target_rows = ctx.saved_tensors
+        dq, dk, dv = attn_bwd(q, k, v, dout.contiguous(), seq_offsets, func, ctx.alpha,
+                              ctx.max_len, target_rows)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def hstu_attention(q, k, v, seq_offsets, func, alpha, max_len, target_rows=None):
+    return HstuAttention.apply(q, k, v, seq_offsets, func, alpha, max_len, target_rows)

@@ -1,0 +1,307 @@
+// C ABI of libhstu_attn.so: argument validation, workspace planning and the
+// launch sequence of each entry point.  Declarations and the full contract are
+// in include/hstu_attn.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "common.h"
+#include "hstu_attn.h"
+
+namespace hstu {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int device_fail(hipError_t e, const char* what) {
+  return fail(HSTU_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int round8(int64_t x) { return (int)((x + kNumXcd - 1) / kNumXcd * kNumXcd); }
+
+bool mfma_path(int dtype, int D) { return dtype == HSTU_BF16 && D == 128; }
+
+}  // namespace
+
+bool plan_workspace(Plan& p, int is_bwd, int dtype, int64_t B, int64_t total, int H, int D,
+                    int nfunc, int targets_only) {
+  (void)dtype;
+  (void)D;
+  p = Plan();
+  if (B < 1 || B > (1 << 24) || total < 0 || total > (int64_t)INT32_MAX || H < 1 || H > 255 ||
+      nfunc < 1 || nfunc > kMaxNfunc)
+    return false;
+  p.ni = (nfunc + 1) / 2;
+  const int64_t nrb = cdiv64(total, kRB) + B;
+  if (nrb > INT32_MAX / 8) return false;
+  p.nrb_cap = (int)nrb;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  p.off_flags = take(64 * sizeof(int));
+  p.off_so = take((size_t)(B + 1) * sizeof(int64_t));
+  p.off_order = take((size_t)B * sizeof(int));
+  p.off_rb = take((size_t)(B + 1) * sizeof(int));
+  p.off_t64 = take((size_t)(B + 1) * sizeof(int));
+  p.off_t128 = take((size_t)(B + 1) * sizeof(int));
+  p.off_env = take((size_t)nrb * p.ni * sizeof(int4));
+  // unit lists: tiles of 128 rows, H per tile
+  const int64_t cap128 = (int64_t)H * (cdiv64(total, 128) + B);
+  p.cap_a = round8(cap128);
+  p.cap_b = is_bwd ? round8(cap128) : 0;
+  p.cap_c = is_bwd ? round8(cap128) : 0;
+  p.off_units_a = take((size_t)p.cap_a * sizeof(int4));
+  p.off_units_b = take((size_t)p.cap_b * sizeof(int4));
+  p.off_units_c = take((size_t)p.cap_c * sizeof(int4));
+  p.partial_bytes = 0;
+  if (targets_only) {
+    const int64_t nchunk = cdiv64(total, targets_chunk_rows()) + B;
+    p.partial_bytes = (size_t)nchunk * H * D * sizeof(float);
+  }
+  p.off_partial = take(p.partial_bytes);
+  p.bytes = off;
+  return true;
+}
+
+Prep prep_view(const Plan& p, void* ws, int B, int64_t total) {
+  char* base = static_cast<char*>(ws);
+  Prep P;
+  P.flags = reinterpret_cast<int*>(base + p.off_flags);
+  P.so = reinterpret_cast<int64_t*>(base + p.off_so);
+  P.order = reinterpret_cast<int*>(base + p.off_order);
+  P.rb_off = reinterpret_cast<int*>(base + p.off_rb);
+  P.tiles64 = reinterpret_cast<int*>(base + p.off_t64);
+  P.tiles128 = reinterpret_cast<int*>(base + p.off_t128);
+  P.env = reinterpret_cast<int4*>(base + p.off_env);
+  P.B = B;
+  P.total = total;
+  P.nrb_cap = p.nrb_cap;
+  return P;
+}
+
+namespace {
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+// Common validation; on success fills the plan.
+int validate(Plan& plan, int is_bwd, int dtype, int64_t B, int64_t total, int H, int D, int nfunc,
+             float alpha, int64_t max_len, const int64_t* seq_offsets, const int32_t* func,
+             const int32_t* target_rows, void* workspace, size_t workspace_bytes) {
+  if (dtype != HSTU_BF16 && dtype != HSTU_FP32)
+    return fail(HSTU_ERR_INVALID, "dtype must be HSTU_BF16 (0) or HSTU_FP32 (1), got %d", dtype);
+  if (B < 1) return fail(HSTU_ERR_INVALID, "B must be >= 1, got %lld", (long long)B);
+  if (B > (1 << 24)) return fail(HSTU_ERR_UNSUPPORTED, "B must be <= 2^24");
+  if (total < 0) return fail(HSTU_ERR_INVALID, "total must be >= 0");
+  if (total > (int64_t)INT32_MAX) return fail(HSTU_ERR_UNSUPPORTED, "total must be < 2^31");
+  if (H < 1) return fail(HSTU_ERR_INVALID, "H must be >= 1, got %d", H);
+  if (H > 255) return fail(HSTU_ERR_UNSUPPORTED, "H must be <= 255, got %d", H);
+  if (D != 32 && D != 64 && D != 128)
+    return fail(HSTU_ERR_UNSUPPORTED, "D must be 32, 64 or 128, got %d", D);
+  if (nfunc < 1 || (nfunc % 2) == 0)
+    return fail(HSTU_ERR_INVALID, "nfunc must be odd and >= 1, got %d", nfunc);
+  if (nfunc > kMaxNfunc)
+    return fail(HSTU_ERR_UNSUPPORTED, "nfunc must be <= %d, got %d", kMaxNfunc, nfunc);
+  if (!isfinite(alpha)) return fail(HSTU_ERR_INVALID, "alpha must be finite");
+  if (max_len < 1) return fail(HSTU_ERR_INVALID, "max_len must be >= 1");
+  if (!seq_offsets) return fail(HSTU_ERR_INVALID, "seq_offsets is NULL");
+  if (!func && total > 0) return fail(HSTU_ERR_INVALID, "func is NULL");
+  if (misaligned(seq_offsets) || misaligned(func) || misaligned(target_rows))
+    return fail(HSTU_ERR_INVALID, "seq_offsets, func and target_rows must be 16-byte aligned");
+  if (!plan_workspace(plan, is_bwd, dtype, B, total, H, D, nfunc, target_rows != nullptr))
+    return fail(HSTU_ERR_UNSUPPORTED, "sizes out of range");
+  if (workspace_bytes < plan.bytes || (!workspace && plan.bytes))
+    return fail(HSTU_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                plan.bytes);
+  if (misaligned(workspace)) return fail(HSTU_ERR_INVALID, "workspace must be 16-byte aligned");
+  return HSTU_OK;
+}
+
+int check_tensor(const void* p, int64_t rows, const char* name) {
+  if (rows > 0 && !p) return fail(HSTU_ERR_INVALID, "%s is NULL", name);
+  if (misaligned(p)) return fail(HSTU_ERR_INVALID, "%s must be 16-byte aligned", name);
+  return HSTU_OK;
+}
+
+Units units_view(void* ws, size_t off, int cap) {
+  Units U;
+  U.list = reinterpret_cast<int4*>(static_cast<char*>(ws) + off);
+  U.cap = cap;
+  return U;
+}
+
+}  // namespace
+
+}  // namespace hstu
+
+using namespace hstu;
+
+extern "C" int hstu_max_nfunc(void) { return kMaxNfunc; }
+
+extern "C" const char* hstu_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" size_t hstu_attn_workspace_size(int is_bwd, int dtype, int64_t B, int64_t total, int H,
+                                           int D, int nfunc, int targets_only) {
+  Plan plan;
+  if (!plan_workspace(plan, is_bwd, dtype, B, total, H, D, nfunc, targets_only)) return 0;
+  return plan.bytes;
+}
+
+extern "C" int hstu_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o,
+                             const int64_t* seq_offsets, int64_t B, int64_t total, int H, int D,
+                             const int32_t* func, int nfunc, float alpha, int64_t max_len,
+                             const int32_t* target_rows, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  Plan plan;
+  int st = validate(plan, 0, dtype, B, total, H, D, nfunc, alpha, max_len, seq_offsets, func,
+                    target_rows, workspace, workspace_bytes);
+  if (st) return st;
+  const int64_t qrows = target_rows ? B : total;
+  if ((st = check_tensor(q, qrows, "q")) || (st = check_tensor(k, total, "k")) ||
+      (st = check_tensor(v, total, "v")) || (st = check_tensor(o, qrows, "o")))
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float inv_max_len = (float)(1.0 / (double)max_len);
+  Prep P = prep_view(plan, workspace, (int)B, total);
+  hipError_t e = launch_prep(P, seq_offsets, target_rows, func, nfunc, s);
+  if (e != hipSuccess) return device_fail(e, "prep");
+  if (target_rows) {
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_partial);
+    Units U = units_view(workspace, plan.off_units_a, plan.cap_a);
+    e = launch_units(P, U, 128, 0, H, kSlotFwdUnits, s);
+    if (e != hipSuccess) return device_fail(e, "unit list");
+    e = launch_targets_fwd(dtype, D, q, k, v, o, P, U, H, func, nfunc, alpha, inv_max_len,
+                           target_rows, partial, s);
+    if (e != hipSuccess) return device_fail(e, "targets-only forward");
+    return HSTU_OK;
+  }
+  if (mfma_path(dtype, D)) {
+    Units U = units_view(workspace, plan.off_units_a, plan.cap_a);
+    e = launch_units(P, U, 128, 1, H, kSlotFwdUnits, s);
+    if (e != hipSuccess) return device_fail(e, "unit list");
+    e = launch_mfma_fwd(q, k, v, o, P, U, H, func, nfunc, alpha, inv_max_len, s);
+  } else {
+    e = launch_generic_fwd(dtype, D, q, k, v, o, P, H, func, nfunc, alpha, inv_max_len, nullptr,
+                           s);
+  }
+  if (e != hipSuccess) return device_fail(e, "forward");
+  return HSTU_OK;
+}
+
+extern "C" int hstu_attn_bwd(int dtype, const void* q, const void* k, const void* v,
+                             const void* dout, void* dq, void* dk, void* dv,
+                             const int64_t* seq_offsets, int64_t B, int64_t total, int H, int D,
+                             const int32_t* func, int nfunc, float alpha, int64_t max_len,
+                             const int32_t* target_rows, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  Plan plan;
+  int st = validate(plan, 1, dtype, B, total, H, D, nfunc, alpha, max_len, seq_offsets, func,
+                    target_rows, workspace, workspace_bytes);
+  if (st) return st;
+  const int64_t qrows = target_rows ? B : total;
+  if ((st = check_tensor(q, qrows, "q")) || (st = check_tensor(k, total, "k")) ||
+      (st = check_tensor(v, total, "v")) || (st = check_tensor(dout, qrows, "dout")) ||
+      (st = check_tensor(dq, qrows, "dq")) || (st = check_tensor(dk, total, "dk")) ||
+      (st = check_tensor(dv, total, "dv")))
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float inv_max_len = (float)(1.0 / (double)max_len);
+  Prep P = prep_view(plan, workspace, (int)B, total);
+  hipError_t e = launch_prep(P, seq_offsets, target_rows, func, nfunc, s);
+  if (e != hipSuccess) return device_fail(e, "prep");
+  if (target_rows) {
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_partial);
+    Units U = units_view(workspace, plan.off_units_a, plan.cap_a);
+    e = launch_units(P, U, 128, 0, H, kSlotFwdUnits, s);
+    if (e != hipSuccess) return device_fail(e, "unit list");
+    e = launch_targets_bwd(dtype, D, q, k, v, dout, dq, dk, dv, P, U, H, func, nfunc, alpha,
+                           inv_max_len, target_rows, partial, s);
+    if (e != hipSuccess) return device_fail(e, "targets-only backward");
+    return HSTU_OK;
+  }
+  if (mfma_path(dtype, D)) {
+    Units Ukv = units_view(workspace, plan.off_units_b, plan.cap_b);
+    Units Uq = units_view(workspace, plan.off_units_c, plan.cap_c);
+    e = launch_units(P, Ukv, 128, 0, H, kSlotKvUnits, s);
+    if (e == hipSuccess) e = launch_units(P, Uq, 128, 1, H, kSlotQUnits, s);
+    if (e != hipSuccess) return device_fail(e, "unit list");
+    e = launch_mfma_bwd(q, k, v, dout, dq, dk, dv, P, Ukv, Uq, H, func, nfunc, alpha,
+                        inv_max_len, s);
+  } else {
+    e = launch_generic_bwd(dtype, D, q, k, v, dout, dq, dk, dv, P, H, func, nfunc, alpha,
+                           inv_max_len, nullptr, s);
+  }
+  if (e != hipSuccess) return device_fail(e, "backward");
+  return HSTU_OK;
+}
+
+extern "C" int hstu_attn_visible_counts(const int64_t* seq_offsets, int64_t B, int64_t total,
+                                        const int32_t* func, int nfunc,
+                                        const int32_t* target_rows, int32_t* counts,
+                                        int64_t* total_pairs, void* stream) {
+  if (B < 1) return fail(HSTU_ERR_INVALID, "B must be >= 1");
+  if (B > (1 << 24) || total > (int64_t)INT32_MAX)
+    return fail(HSTU_ERR_UNSUPPORTED, "sizes out of range");
+  if (total < 0) return fail(HSTU_ERR_INVALID, "total must be >= 0");
+  if (nfunc < 1 || (nfunc % 2) == 0)
+    return fail(HSTU_ERR_INVALID, "nfunc must be odd and >= 1, got %d", nfunc);
+  if (nfunc > kMaxNfunc)
+    return fail(HSTU_ERR_UNSUPPORTED, "nfunc must be <= %d, got %d", kMaxNfunc, nfunc);
+  if (!seq_offsets) return fail(HSTU_ERR_INVALID, "seq_offsets is NULL");
+  if (!func && total > 0) return fail(HSTU_ERR_INVALID, "func is NULL");
+  hipError_t e = launch_visible_counts(seq_offsets, (int)B, total, func, nfunc, target_rows,
+                                       counts, total_pairs, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(e, "visible counts");
+  return HSTU_OK;
+}
+
+extern "C" int hstu_attn_check_inputs(const int64_t* seq_offsets, int64_t B, int64_t total,
+                                      const int32_t* target_rows, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (B < 1) return fail(HSTU_ERR_INVALID, "B must be >= 1");
+  if (total < 0) return fail(HSTU_ERR_INVALID, "total must be >= 0");
+  if (!seq_offsets) return fail(HSTU_ERR_INVALID, "seq_offsets is NULL");
+  if (misaligned(seq_offsets) || misaligned(target_rows))
+    return fail(HSTU_ERR_INVALID, "seq_offsets and target_rows must be 16-byte aligned");
+  Plan plan;
+  if (!plan_workspace(plan, 0, HSTU_BF16, B, total, 1, 128, 1, 0))
+    return fail(HSTU_ERR_UNSUPPORTED, "sizes out of range");
+  if (workspace_bytes < plan.bytes || !workspace)
+    return fail(HSTU_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                plan.bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Prep P = prep_view(plan, workspace, (int)B, total);
+  hipError_t e = launch_prep(P, seq_offsets, target_rows, nullptr, 1, s);
+  if (e != hipSuccess) return device_fail(e, "prep");
+  int flags = 0;
+  e = hipMemcpyAsync(&flags, P.flags, sizeof(int), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return device_fail(e, "reading validation flags");
+  if (flags) {
+    return fail(HSTU_ERR_INPUT, "malformed device input:%s%s%s%s",
+                (flags & kFlagOffsetsStart) ? " seq_offsets[0] != 0;" : "",
+                (flags & kFlagOffsetsEnd) ? " seq_offsets[B] != total;" : "",
+                (flags & kFlagOffsetsOrder) ? " seq_offsets decreasing or out of range;" : "",
+                (flags & kFlagTargetRange) ? " target row outside its sequence;" : "");
+  }
+  return HSTU_OK;
+}

@@ -1,0 +1,233 @@
+// Internal declarations shared by the HIP sources of libhstu_attn.so (gfx950).
+//
+// Terms used throughout:
+//   so[B+1]    sanitized sequence offsets (int64): so[0] = 0, nondecreasing,
+//              so[B] = total; equal to seq_offsets for well-formed input.
+//   row block  RB = 64 consecutive query rows of one sequence; the interval
+//              decoder summarizes the func bounds of each row block.
+//   envelope   per row block and interval j: union bounds [ulo, uhi) (smallest
+//              start / largest end over rows whose clipped interval j is not
+//              empty) and intersection bounds [ilo, ihi) (largest start /
+//              smallest end over all valid rows; empty unless every row has a
+//              non-empty interval j).  A key tile that meets no union envelope is
+//              skipped; one inside an intersection envelope needs no mask.
+//   unit       one workgroup's work item {b, tile, h}; unit lists are built on
+//              the device, sequences ordered longest first and dealt across the
+//              8 XCDs so each XCD gets a balanced share and keeps a sequence's
+//              tiles (which re-read the same K/V) in its own L2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+constexpr int kRB = 64;          // rows per row block (decoder granularity)
+constexpr int kMaxNfunc = 9;     // largest nfunc accepted
+constexpr int kMaxNI = (kMaxNfunc + 1) / 2;  // largest number of intervals
+constexpr int kHistBins = 4096;  // length buckets of the scheduler's counting sort
+constexpr int kNumXcd = 8;       // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// error flags written by the preparation kernel (bit set = problem seen)
+enum : int {
+  kFlagOffsetsStart = 1,   // seq_offsets[0] != 0
+  kFlagOffsetsEnd = 2,     // seq_offsets[B] != total
+  kFlagOffsetsOrder = 4,   // decreasing or out of [0, total]
+  kFlagTargetRange = 8,    // a target row outside [0, L_b)
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Slots of Prep::flags holding unit counts written by the unit-list kernel.
+constexpr int kSlotFwdUnits = 4, kSlotKvUnits = 5, kSlotQUnits = 6;
+
+// Device pointers into the caller's workspace (laid out by plan_workspace).
+struct Prep {
+  int* flags;          // [16]: [0] error bits, [1] units of tile 64, [2] units of tile 128
+  int64_t* so;         // [B+1] sanitized offsets
+  int* order;          // [B] sequences: longest first, dealt over the XCDs
+  int* rb_off;         // [B+1] first row block of each sequence (original order)
+  int* tiles64;        // [B+1] prefix over `order` of ceil(L/64)
+  int* tiles128;       // [B+1] prefix over `order` of ceil(L/128)
+  int4* env;           // [nrb_cap * ni] envelopes {ulo, uhi, ilo, ihi}
+  int B;
+  int64_t total;
+  int nrb_cap;         // capacity of row blocks: ceil(total/64) + B
+};
+
+struct Units {
+  int4* list;  // {b, tile, h, 0}; b < 0 marks an unused slot
+  int cap;     // entries (multiple of 8)
+};
+
+// ---------------------------------------------------------------------------
+// host-side planning
+// ---------------------------------------------------------------------------
+struct Plan {
+  size_t bytes = 0;
+  size_t off_flags, off_so, off_order, off_rb, off_t64, off_t128, off_env;
+  size_t off_units_a, off_units_b, off_units_c;  // unit lists (kernel specific)
+  size_t off_partial;                             // targets-only partial sums
+  int cap_a = 0, cap_b = 0, cap_c = 0;
+  int nrb_cap = 0;
+  int ni = 0;
+  size_t partial_bytes = 0;
+};
+
+// Fills `plan` for a call; returns false if sizes are out of range.
+bool plan_workspace(Plan& plan, int is_bwd, int dtype, int64_t B, int64_t total, int H, int D,
+                    int nfunc, int targets_only);
+Prep prep_view(const Plan& plan, void* ws, int B, int64_t total);
+
+// ---------------------------------------------------------------------------
+// launchers (each returns a hipError_t from the launch)
+// ---------------------------------------------------------------------------
+hipError_t launch_prep(const Prep& P, const int64_t* seq_offsets, const int32_t* target_rows,
+                       const int32_t* func, int nfunc, hipStream_t stream);
+hipError_t launch_units(const Prep& P, const Units& U, int tile, int descending, int H,
+                        int count_slot, hipStream_t stream);
+hipError_t launch_visible_counts(const int64_t* seq_offsets, int B, int64_t total,
+                                 const int32_t* func, int nfunc, const int32_t* target_rows,
+                                 int32_t* counts, int64_t* total_pairs, hipStream_t stream);
+
+// generic fp32-FMA kernels (any supported dtype and D)
+hipError_t launch_generic_fwd(int dtype, int D, const void* q, const void* k, const void* v,
+                              void* o, const Prep& P, int H, const int32_t* func, int nfunc,
+                              float alpha, float inv_max_len, const int32_t* target_rows,
+                              hipStream_t stream);
+hipError_t launch_generic_bwd(int dtype, int D, const void* q, const void* k, const void* v,
+                              const void* dout, void* dq, void* dk, void* dv, const Prep& P,
+                              int H, const int32_t* func, int nfunc, float alpha,
+                              float inv_max_len, const int32_t* target_rows, hipStream_t stream);
+
+// bf16, D = 128 MFMA kernels (full-length mode)
+hipError_t launch_mfma_fwd(const void* q, const void* k, const void* v, void* o, const Prep& P,
+                           const Units& U, int H, const int32_t* func, int nfunc, float alpha,
+                           float inv_max_len, hipStream_t stream);
+hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const void* dout,
+                           void* dq, void* dk, void* dv, const Prep& P, const Units& Ukv,
+                           const Units& Uq, int H, const int32_t* func, int nfunc, float alpha,
+                           float inv_max_len, hipStream_t stream);
+
+// targets-only streaming kernels (any dtype, D); U lists 128-row key tiles
+int targets_chunk_rows();
+hipError_t launch_targets_fwd(int dtype, int D, const void* q, const void* k, const void* v,
+                              void* o, const Prep& P, const Units& U, int H, const int32_t* func,
+                              int nfunc, float alpha, float inv_max_len,
+                              const int32_t* target_rows, float* partial, hipStream_t stream);
+hipError_t launch_targets_bwd(int dtype, int D, const void* q, const void* k, const void* v,
+                              const void* dout, void* dq, void* dk, void* dv, const Prep& P,
+                              const Units& U, int H, const int32_t* func, int nfunc, float alpha,
+                              float inv_max_len, const int32_t* target_rows, float* partial,
+                              hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+
+// Workgroup index -> position in a unit list whose XCD shares are contiguous.
+// Workgroup i runs on XCD i % 8; with n valid units, XCD x takes positions
+// [x*per, (x+1)*per), per = ceil(n / 8).  Returns -1 for idle workgroups.
+__device__ __forceinline__ int xcd_slot(int bid, int n) {
+  int per = (n + kNumXcd - 1) / kNumXcd;
+  int k = bid / kNumXcd;
+  int slot = (bid % kNumXcd) * per + k;
+  return (k < per && slot < n) ? slot : -1;
+}
+
+// Largest index i in [0, n] with a[i] <= x (a nondecreasing, a[0] <= x).
+template <typename T>
+__device__ __forceinline__ int upper_index(const T* a, int n, T x) {
+  int lo = 0, hi = n;  // invariant: a[lo] <= x, answer in [lo, hi]
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Clipped interval j of the row whose func column is `col`: [lo, hi) within
+// [0, L); an empty interval is returned as lo = L, hi = 0 (so that min/max
+// reductions of starts and ends ignore it).
+__device__ __forceinline__ void row_interval(const int32_t* func, int64_t total, int64_t col,
+                                             int j, int L, int& lo, int& hi) {
+  int a, b;
+  if (j == 0) {
+    a = 0;
+    b = func[col];
+  } else {
+    a = func[(int64_t)(2 * j - 1) * total + col];
+    b = func[(int64_t)(2 * j) * total + col];
+  }
+  a = max(a, 0);
+  b = min(b, L);
+  if (b <= a) { a = L; b = 0; }
+  lo = a;
+  hi = b;
+}
+
+// Visible columns of one row as sorted, disjoint intervals (union of the
+// clipped func intervals).  Returns the number of intervals written.
+__device__ __forceinline__ int merged_intervals(const int32_t* func, int64_t total, int64_t col,
+                                                int nfunc, int L, int* lo, int* hi) {
+  const int ni = (nfunc + 1) / 2;
+  int m = 0;
+  for (int j = 0; j < ni; ++j) {
+    int a, c;
+    row_interval(func, total, col, j, L, a, c);
+    if (c > a) {
+      int k = m++;
+      while (k > 0 && lo[k - 1] > a) {
+        lo[k] = lo[k - 1];
+        hi[k] = hi[k - 1];
+        --k;
+      }
+      lo[k] = a;
+      hi[k] = c;
+    }
+  }
+  int w = 0;
+  for (int k = 0; k < m; ++k) {
+    if (w > 0 && lo[k] <= hi[w - 1]) {
+      hi[w - 1] = max(hi[w - 1], hi[k]);
+    } else {
+      lo[w] = lo[k];
+      hi[w] = hi[k];
+      ++w;
+    }
+  }
+  return w;
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j supplies the address of 4 consecutive 16-bit values M[j][0..3]; lane i
+// receives M[i/4 + 4t][i%4] for t = 0..3.  If the 16 lanes address a 4 x 16
+// block of a row-major matrix A -- lane j at &A[r0 + j/4][c0 + 4*(j%4)] -- lane i
+// receives A[r0 + t][c0 + i], t = 0..3: four consecutive rows of one column,
+// which is the K-contiguous operand layout the MFMA wants.
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(((uint32_t)x) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  __bf16 b = (__bf16)x;  // round to nearest even (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// SiLU pieces on the fast transcendental units: logistic(a*x) with
+// c = -a*log2(e) precomputed.  v_exp_f32 / v_rcp_f32 are accurate to ~1 ulp;
+// overflow of the exponent gives rcp(inf) = 0, the correct limit.
+__device__ __forceinline__ float logistic_scaled(float x, float c) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(c * x));
+}
+
+}  // namespace hstu

@@ -1,0 +1,206 @@
+// Forward kernel, bf16 inputs, D = 128, bf16 MFMA (v_mfma_f32_32x32x16_bf16).
+//
+//   O_i = (alpha / max_len) * sum_{j in V_i} y_ij v_j,  y_ij = x_ij * logistic(alpha x_ij),
+//   x_ij = <q_i, k_j>   (so that alpha * y_ij = silu(alpha x_ij)).
+//
+// One workgroup (4 waves) owns 128 query rows of one (sequence, head); wave w
+// owns rows [32w, 32w+32) of the tile.  The workgroup walks the key tiles of
+// 64 columns that its row blocks' interval envelopes reach (the rest are never
+// loaded), in increasing order:
+//   1. K and V tiles -> LDS, both row-major, staged through registers so the
+//      next tile's global loads overlap this tile's math;
+//   2. S^T = K Q^T on MFMA: A = K from LDS, B = Q^T from registers (each lane
+//      keeps its query row's 128 dims), so the accumulator holds one query row
+//      per lane and 16 key columns;
+//   3. y = x * logistic(alpha x) in registers (v_exp_f32, v_rcp_f32), the
+//      interval mask applied only on tiles that some row sees partially, then
+//      rounded to bf16 -- already in the B-operand layout of the next product;
+//   4. O^T += V^T Y^T on MFMA: A = V^T read from the row-major V tile with the
+//      LDS transpose read, B = Y^T from registers.
+// The key index order inside each 16-wide MFMA step is permuted identically
+// in both operands (it is a sum), which is what lets step 3 feed step 4
+// without any data movement.
+#include "common.h"
+#include "tiles.h"
+
+namespace hstu {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBM = 128;             // query rows per workgroup
+constexpr int kBN = 64;              // key columns per tile
+constexpr int kKStr = kD + 8;        // LDS row stride of K (bf16): 272 B, spreads banks
+constexpr int kVStr = kD + 16;       // LDS row stride of V (bf16): 288 B, for transpose reads
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, Prep P, const int4* __restrict__ units,
+    const int* __restrict__ unit_count, int H, const int32_t* __restrict__ func, int nfunc,
+    float alpha, float out_scale) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kBN * kKStr];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kBN * kVStr];
+
+  const int slot = xcd_slot(blockIdx.x, *unit_count);
+  if (slot < 0) return;
+  const int4 u = units[slot];
+  const int b = u.x, qt = u.y, h = u.z;
+  const int64_t s = P.so[b];
+  const int L = (int)(P.so[b + 1] - s);
+  const int r0 = qt * kBM;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, g = lane >> 5;
+  const int ni = (nfunc + 1) / 2;
+  const int64_t rs = (int64_t)H * kD;  // row stride (elements)
+
+  // this lane's query row (B-operand column n of wave `wave`)
+  const int row = r0 + wave * 32 + n;
+  const bool row_ok = row < L;
+  bf16x8 qf[kD / 16];
+  {
+    const uint16_t* qp = q + (s + row) * rs + (int64_t)h * kD + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      if (row_ok) {
+        qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+      } else {
+        qf[ks] = bf16x8{};
+      }
+    }
+  }
+  int lo[kMaxNI], hi[kMaxNI];
+#pragma unroll
+  for (int j = 0; j < kMaxNI; ++j) {
+    lo[j] = L;
+    hi[j] = 0;
+    if (j < ni && row_ok) row_interval(func, P.total, s + row, j, L, lo[j], hi[j]);
+  }
+
+  TileRanges R;
+  tile_ranges(P, b, r0, kBM, L, ni, kBN, R);
+
+  f32x16 oacc[kD / 32];
+#pragma unroll
+  for (int mb = 0; mb < kD / 32; ++mb) oacc[mb] = f32x16{};
+
+  const float c_exp = -alpha * kLog2e;
+
+  // staging registers for one K/V tile: rows krow + 16i, dims kcol..kcol+7
+  const int krow = tid >> 4, kcol = (tid & 15) * 8;
+  uint4 kreg[4], vreg[4];
+  auto load_tile = [&](int t) {
+    const int c0 = t * kBN;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kv = krow + 16 * i;
+      kreg[i] = make_uint4(0, 0, 0, 0);
+      if (c0 + kv < L)
+        kreg[i] = *reinterpret_cast<const uint4*>(k + (s + c0 + kv) * rs + (int64_t)h * kD + kcol);
+      vreg[i] = make_uint4(0, 0, 0, 0);
+      if (c0 + kv < L)
+        vreg[i] = *reinterpret_cast<const uint4*>(v + (s + c0 + kv) * rs + (int64_t)h * kD + kcol);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4*>(&sK[(krow + 16 * i) * kKStr + kcol]) = kreg[i];
+      *reinterpret_cast<uint4*>(&sV[(krow + 16 * i) * kVStr + kcol]) = vreg[i];
+    }
+  };
+  // transpose-read addressing for the A operand V^T: lane j of each 16-lane
+  // group points at row j/4 of a 4-row block, columns 4*(j%4)..+3
+  const int grp = lane >> 4, gl = lane & 15;
+  const uint16_t* vbase = &sV[(4 * (grp >> 1) + (gl >> 2)) * kVStr + (grp & 1) * 16 + 4 * (gl & 3)];
+
+  int t = next_live(R, ni, 0);
+  if (t >= 0) {
+    load_tile(t);
+    store_tile();
+  }
+  __syncthreads();
+  while (t >= 0) {
+    const int tn = next_live(R, ni, t + 1);
+    if (tn >= 0) load_tile(tn);
+    const int c0 = t * kBN;
+    const bool full = tile_full(R, ni, c0, min(c0 + kBN, L));
+
+    // S^T = K Q^T for the 64 columns (two 32-column halves)
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
+      const uint16_t* kp = &sK[(kb * 32 + n) * kKStr + g * 8];
+#pragma unroll
+      for (int ks = 0; ks < kD / 16; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + ks * 16);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb], 0, 0, 0);
+      }
+    }
+    // y = x * logistic(alpha x), masked, -> bf16 B operands
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      uint32_t mg = 0xffffffffu;
+      if (!full) mg = col_mask32(lo, hi, ni, c0 + kb * 32) >> (g * 4);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = sacc[kb][r];
+        float y = x * logistic_scaled(x, c_exp);
+        const int bit = (r >> 2) * 8 + (r & 3);
+        if (!((mg >> bit) & 1u)) y = 0.f;
+        pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)y;
+      }
+    }
+    // O^T += V^T Y^T
+    // A = V^T: lane (d = mb*32 + n, half g) takes key rows 16ss + 4g + {0..3}
+    // and 16ss + 8 + 4g + {0..3}, the same order the Y^T operand uses.
+#pragma unroll
+    for (int ss = 0; ss < 4; ++ss) {
+#pragma unroll
+      for (int mb = 0; mb < kD / 32; ++mb) {
+        const uint16_t* vp = vbase + (16 * ss) * kVStr + mb * 32;
+        const bf16x4 lo4 = lds_read_tr(vp);
+        const bf16x4 hi4 = lds_read_tr(vp + 8 * kVStr);
+        const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ss], oacc[mb], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    if (tn >= 0) store_tile();
+    __syncthreads();
+    t = tn;
+  }
+
+  // epilogue: lane holds O[row][mb*32 + j*8 + g*4 + 0..3]
+  if (row_ok) {
+    uint16_t* op = o + (s + row) * rs + (int64_t)h * kD + g * 4;
+#pragma unroll
+    for (int mb = 0; mb < kD / 32; ++mb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 w4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w4[i] = (__bf16)(oacc[mb][j * 4 + i] * out_scale);
+        *reinterpret_cast<bf16x4*>(op + mb * 32 + j * 8) = w4;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mfma_fwd(const void* q, const void* k, const void* v, void* o, const Prep& P,
+                           const Units& U, int H, const int32_t* func, int nfunc, float alpha,
+                           float inv_max_len, hipStream_t stream) {
+  if (U.cap == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fwd_bf16, dim3(U.cap), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), P, U.list,
+                     P.flags + 4, H, func, nfunc, alpha, alpha * inv_max_len);
+  return hipGetLastError();
+}
+
+}  // namespace hstu

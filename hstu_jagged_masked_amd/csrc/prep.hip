@@ -1,0 +1,316 @@
+// Preparation kernels: sanitized offsets, the jagged tile scheduler (longest
+// sequences first, dealt over the XCDs), per-row-block interval envelopes,
+// and exact per-row visible-column counts.
+//
+// The interval semantics follow TorchEasyRec PR #670 ("What changed"):
+// interval 0 = [0, f0), interval j = [f(2j-1), f(2j)), empty when end <= start,
+// visible set = union, bounds sequence-local and clipped to [0, L).
+#include "common.h"
+
+namespace hstu {
+
+namespace {
+
+constexpr int kPrepThreads = 1024;
+constexpr int kPrepWaves = kPrepThreads / 64;
+
+struct SumOp {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct MaxOp {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a > b ? a : b; }
+};
+
+// Inclusive scan of one value per thread across the 1024-thread block.
+// `scratch` holds kPrepWaves entries.  Returns the inclusive prefix; *total
+// receives the block-wide reduction.
+template <typename T, typename Op>
+__device__ T block_inclusive_scan(T x, T* scratch, T* total, Op op) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int s = 1; s < 64; s <<= 1) {
+    T y = __shfl_up(x, s, 64);
+    if (lane >= s) x = op(x, y);
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kPrepWaves; ++w) scratch[w] = op(scratch[w - 1], scratch[w]);
+  }
+  __syncthreads();
+  if (wave > 0) x = op(scratch[wave - 1], x);
+  *total = scratch[kPrepWaves - 1];
+  __syncthreads();
+  return x;
+}
+
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Position of sorted rank p after snake-dealing B ranks over 8 bins and
+// concatenating the bins (bin 0 first).  Within a bin, ranks keep their order.
+__device__ int dealt_position(int p, int B) {
+  const int R = B / kNumXcd, rem = B % kNumXcd;
+  int round = p / kNumXcd, pos = p % kNumXcd;
+  int bin = (round & 1) ? (kNumXcd - 1 - pos) : pos;
+  int start = 0;
+  for (int x = 0; x < bin; ++x) {
+    int n = R;
+    if (rem) {
+      bool extra = (R & 1) ? (x >= kNumXcd - rem) : (x < rem);
+      n += extra ? 1 : 0;
+    }
+    start += n;
+  }
+  return start + round;
+}
+
+__global__ __launch_bounds__(kPrepThreads) void k_prep(Prep P, const int64_t* __restrict__ off,
+                                                       const int32_t* __restrict__ target_rows) {
+  __shared__ int hist[kHistBins];
+  __shared__ int64_t scan64[kPrepWaves];
+  __shared__ int scan32[kPrepWaves];
+  __shared__ int sflags;
+  const int tid = threadIdx.x;
+  const int B = P.B;
+  const int64_t total = P.total;
+  if (tid == 0) sflags = 0;
+  for (int i = tid; i < kHistBins; i += kPrepThreads) hist[i] = 0;
+  __syncthreads();
+
+  // 1. sanitized offsets: clamp into [0, total] and take a running maximum.
+  int flags = 0;
+  int64_t run = 0;
+  for (int base = 0; base <= B; base += kPrepThreads) {
+    const int b = base + tid;
+    int64_t x = 0;
+    if (b <= B) {
+      int64_t raw = off[b];
+      if (b == 0 && raw != 0) flags |= kFlagOffsetsStart;
+      if (b == B && raw != total) flags |= kFlagOffsetsEnd;
+      if (raw < 0 || raw > total) flags |= kFlagOffsetsOrder;
+      if (b > 0 && raw < off[b - 1]) flags |= kFlagOffsetsOrder;
+      x = raw < 0 ? 0 : (raw > total ? total : raw);
+    }
+    int64_t chunk_max;
+    int64_t m = block_inclusive_scan(x, scan64, &chunk_max, MaxOp());
+    m = m > run ? m : run;
+    if (b == 0) m = 0;
+    if (b == B) m = total;
+    if (b <= B) P.so[b] = m;
+    run = chunk_max > run ? chunk_max : run;
+  }
+  __syncthreads();
+
+  // 2. lengths -> histogram keyed by decreasing length; target-row checks.
+  for (int b = tid; b < B; b += kPrepThreads) {
+    const int L = (int)(P.so[b + 1] - P.so[b]);
+    if (target_rows) {
+      const int t = target_rows[b];
+      if (L > 0 && (t < 0 || t >= L)) flags |= kFlagTargetRange;
+    }
+    const int bucket = min(L >> 4, kHistBins - 1);
+    atomicAdd(&hist[kHistBins - 1 - bucket], 1);
+  }
+  __syncthreads();
+
+  // 3. exclusive scan of the histogram (4 bins per thread).
+  {
+    int v[4], s = 0;
+    for (int i = 0; i < 4; ++i) { v[i] = hist[tid * 4 + i]; s += v[i]; }
+    int tot;
+    int incl = block_inclusive_scan(s, scan32, &tot, SumOp());
+    int run_bin = incl - s;
+    for (int i = 0; i < 4; ++i) { hist[tid * 4 + i] = run_bin; run_bin += v[i]; }
+  }
+  __syncthreads();
+
+  // 4. scatter: sorted rank from the bucket cursor, then dealt position.
+  for (int b = tid; b < B; b += kPrepThreads) {
+    const int L = (int)(P.so[b + 1] - P.so[b]);
+    const int bucket = min(L >> 4, kHistBins - 1);
+    const int rank = atomicAdd(&hist[kHistBins - 1 - bucket], 1);
+    P.order[dealt_position(rank, B)] = b;
+  }
+  __syncthreads();
+
+  // 5. row-block offsets (original order) and tile prefixes (dealt order).
+  int carry_rb = 0, carry64 = 0, carry128 = 0;
+  for (int base = 0; base < B; base += kPrepThreads) {
+    const int b = base + tid;
+    int nrb = 0, n64 = 0, n128 = 0;
+    if (b < B) {
+      const int L = (int)(P.so[b + 1] - P.so[b]);
+      nrb = cdiv(L, kRB);
+      const int sb = P.order[b];
+      const int Ls = (int)(P.so[sb + 1] - P.so[sb]);
+      n64 = cdiv(Ls, 64);
+      n128 = cdiv(Ls, 128);
+    }
+    int t_rb, t64, t128;
+    int i_rb = block_inclusive_scan(nrb, scan32, &t_rb, SumOp());
+    int i64 = block_inclusive_scan(n64, scan32, &t64, SumOp());
+    int i128 = block_inclusive_scan(n128, scan32, &t128, SumOp());
+    if (b < B) {
+      P.rb_off[b] = carry_rb + i_rb - nrb;
+      P.tiles64[b] = carry64 + i64 - n64;
+      P.tiles128[b] = carry128 + i128 - n128;
+    }
+    carry_rb += t_rb;
+    carry64 += t64;
+    carry128 += t128;
+  }
+  if (tid == 0) {
+    P.rb_off[B] = carry_rb;
+    P.tiles64[B] = carry64;
+    P.tiles128[B] = carry128;
+  }
+  if (flags) atomicOr(&sflags, flags);
+  __syncthreads();
+  if (tid == 0) {
+    P.flags[0] = sflags;
+    P.flags[3] = carry_rb;
+  }
+}
+
+// Unit list for tiles of `tile` rows: sequence p (dealt order) owns the slots
+// [H*T[p], H*T[p+1]); within it head-major, tiles in decreasing index when
+// `descending` (heaviest first for prefix-like masks), else increasing.
+__global__ void k_units(Prep P, Units U, int tile, int descending, int H, int count_slot) {
+  const int lam = blockIdx.x * blockDim.x + threadIdx.x;
+  const int* T = tile == 64 ? P.tiles64 : P.tiles128;
+  const int B = P.B;
+  const int n = H * T[B];
+  if (lam == 0) P.flags[count_slot] = n;
+  if (lam >= U.cap) return;
+  if (lam >= n) {
+    U.list[lam] = make_int4(-1, 0, 0, 0);
+    return;
+  }
+  const int p = upper_index(T, B, lam / H);
+  const int nt = T[p + 1] - T[p];
+  const int r = lam - H * T[p];
+  const int h = r / nt;
+  const int tr = r - h * nt;
+  U.list[lam] = make_int4(P.order[p], descending ? nt - 1 - tr : tr, h, 0);
+}
+
+// One wave per row block: envelopes of every interval.
+__global__ __launch_bounds__(64) void k_envelopes(Prep P, const int32_t* __restrict__ func,
+                                                  int nfunc) {
+  const int g = blockIdx.x;
+  const int nrb = P.rb_off[P.B];
+  if (g >= nrb) return;
+  const int b = upper_index(P.rb_off, P.B, g);
+  const int rb = g - P.rb_off[b];
+  const int64_t s = P.so[b];
+  const int L = (int)(P.so[b + 1] - s);
+  const int i = rb * kRB + threadIdx.x;
+  const bool valid = i < L;
+  const int ni = (nfunc + 1) / 2;
+  for (int j = 0; j < ni; ++j) {
+    int lo = L, hi = 0;
+    if (valid) row_interval(func, P.total, s + i, j, L, lo, hi);
+    int ulo = lo, uhi = hi;
+    int ilo = valid ? lo : INT32_MIN, ihi = valid ? hi : INT32_MAX;
+    for (int m = 1; m < 64; m <<= 1) {
+      ulo = min(ulo, __shfl_xor(ulo, m, 64));
+      uhi = max(uhi, __shfl_xor(uhi, m, 64));
+      ilo = max(ilo, __shfl_xor(ilo, m, 64));
+      ihi = min(ihi, __shfl_xor(ihi, m, 64));
+    }
+    if (threadIdx.x == 0) P.env[(int64_t)g * ni + j] = make_int4(ulo, uhi, ilo, ihi);
+  }
+}
+
+__global__ void k_zero_i64(int64_t* p) { *p = 0; }
+
+// |V_i| per row (or per candidate): union of up to kMaxNI clipped intervals.
+__global__ void k_visible_counts(const int64_t* __restrict__ off, int B, int64_t total,
+                                 const int32_t* __restrict__ func, int nfunc,
+                                 const int32_t* __restrict__ target_rows, int32_t* counts,
+                                 unsigned long long* total_pairs) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int n = 0;
+  bool active;
+  if (target_rows) {
+    active = t < B;
+  } else {
+    active = t < total;
+  }
+  if (active) {
+    int b;
+    int64_t row;
+    if (target_rows) {
+      b = (int)t;
+    } else {
+      b = upper_index(off, B, t);
+      if (b >= B) b = B - 1;
+    }
+    int64_t start = off[b];
+    start = start < 0 ? 0 : (start > total ? total : start);
+    int64_t end = off[b + 1];
+    end = end < start ? start : (end > total ? total : end);
+    const int L = (int)(end - start);
+    if (target_rows) {
+      row = target_rows[b];
+    } else {
+      row = t - start;
+    }
+    if (row >= 0 && row < L) {
+      int lo[kMaxNI], hi[kMaxNI];
+      const int m = merged_intervals(func, total, start + row, nfunc, L, lo, hi);
+      for (int k = 0; k < m; ++k) n += hi[k] - lo[k];
+    }
+    if (counts) counts[t] = n;
+  }
+  if (total_pairs) {
+    unsigned long long s = (unsigned long long)n;
+    for (int m = 1; m < 64; m <<= 1) s += __shfl_xor(s, m, 64);
+    if ((threadIdx.x & 63) == 0 && s) atomicAdd(total_pairs, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prep(const Prep& P, const int64_t* seq_offsets, const int32_t* target_rows,
+                       const int32_t* func, int nfunc, hipStream_t stream) {
+  hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, stream, P, seq_offsets, target_rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || func == nullptr) return e;
+  if (P.nrb_cap > 0) {
+    hipLaunchKernelGGL(k_envelopes, dim3(P.nrb_cap), dim3(64), 0, stream, P, func, nfunc);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_units(const Prep& P, const Units& U, int tile, int descending, int H,
+                        int count_slot, hipStream_t stream) {
+  const int threads = 256;
+  const int blocks = (U.cap + threads - 1) / threads;
+  hipLaunchKernelGGL(k_units, dim3(blocks > 0 ? blocks : 1), dim3(threads), 0, stream, P, U, tile,
+                     descending, H, count_slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_visible_counts(const int64_t* seq_offsets, int B, int64_t total,
+                                 const int32_t* func, int nfunc, const int32_t* target_rows,
+                                 int32_t* counts, int64_t* total_pairs, hipStream_t stream) {
+  if (total_pairs) {
+    hipLaunchKernelGGL(k_zero_i64, dim3(1), dim3(1), 0, stream, total_pairs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n = target_rows ? (int64_t)B : total;
+  if (n == 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(k_visible_counts, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     seq_offsets, B, total, func, nfunc, target_rows, counts,
+                     reinterpret_cast<unsigned long long*>(total_pairs));
+  return hipGetLastError();
+}
+
+}  // namespace hstu

@@ -1,0 +1,129 @@
+/*
+ * hstu_attn.h -- C ABI of the MI355X (gfx950) HSTU jagged masked attention
+ * library (libhstu_attn.so).
+ *
+ * The operator.  Sequences are stored jagged: sequence b owns the global rows
+ * [seq_offsets[b], seq_offsets[b+1]) of every [rows, H, D] tensor, and all row
+ * and column indices below are local to their sequence.  Each query row i
+ * carries a column mask given by `func`, the int32 interval encoding of
+ * TorchEasyRec PR #670 ("move the HSTU arbitrary-mask path to NFUNC=5",
+ * sections "Why" and "What changed"):
+ *     interval 0 = [0, f0),  interval j = [f(2j-1), f(2j))  for j = 1..(nfunc-1)/2,
+ * a pair whose end is <= its start is empty and skipped, and the visible set
+ * V_i is the union of the intervals clipped to [0, L_b).  Any int32 value is
+ * legal (it is clipped); func is shared by all heads (the review reply on that
+ * PR shows the head dimension of func is never read), so it has no head axis.
+ * For a visible pair (i, j) of head h:
+ *     P_ij = alpha * <q_i, k_j>,   S_ij = silu(P_ij) / max_len,
+ *     O_i  = sum_{j in V_i} S_ij v_j,
+ * and the backward, with silu'(x) = s(x)(1 + x(1 - s(x))), s the logistic:
+ *     dP_ij = <dO_i, v_j> silu'(P_ij) / max_len,
+ *     dQ_i = alpha sum_j dP_ij k_j,  dK_j = alpha sum_i dP_ij q_i,
+ *     dV_j = sum_i S_ij dO_i.
+ * Rows with no visible column get O = dQ = 0; key rows no query sees get
+ * dK = dV = 0 (always written).
+ *
+ * Targets-only mode (MLCommons training PR #903, "Summary" and "Gating"):
+ * exactly one candidate row per sequence, i_b = target_rows[b], forms Q
+ * against the full-length K and V.  Then q, o, dO and dq are compact [B, H, D]
+ * (row b = candidate of sequence b) while k, v, dk, dv stay [total, H, D]; the
+ * candidate's mask is func column seq_offsets[b] + i_b.  dK/dV rows that the
+ * candidate does not see are written as 0.
+ *
+ * Layouts.  q, k, v, o, dout, dq, dk, dv: row-major [rows, H, D] (D fastest),
+ * elements bf16 (HSTU_BF16) or fp32 (HSTU_FP32), 16-byte aligned.  func:
+ * int32 [nfunc, total] row-major (column t = global row t).  seq_offsets:
+ * int64 [B+1], seq_offsets[0] = 0, nondecreasing, seq_offsets[B] = total
+ * (the "complete cumsum" of the lengths).  target_rows: int32 [B].  Every
+ * pointer is a DEVICE pointer, except that `total_pairs` below is too.
+ *
+ * Supported: B >= 1, total >= 0, 1 <= H <= 255, D in {32, 64, 128},
+ * 1 <= nfunc <= hstu_max_nfunc() and odd, max_len >= 1, alpha finite.
+ * bf16 with D = 128 runs the MFMA kernels; the other combinations run plain
+ * fp32 FMA kernels (correct at any size, tuned for none).
+ *
+ * Ownership.  The caller allocates and owns every buffer, including the
+ * workspace (size from hstu_attn_workspace_size).  The library keeps no
+ * pointer after a call returns and allocates no device memory itself.  Work is
+ * enqueued on `stream` (a hipStream_t passed as void*; NULL = the default
+ * stream) and runs asynchronously; buffers must stay valid until it completes.
+ *
+ * Errors.  Every entry point validates its arguments on the host before
+ * enqueueing anything and returns a status; on failure nothing is enqueued and
+ * hstu_last_error() describes the problem.  The library never aborts.  Device
+ * contents (offsets, target rows) are not read by the host: kernels clamp them
+ * into range, so malformed offsets give wrong results but no out-of-bounds
+ * access; hstu_attn_check_inputs() reports them.
+ */
+#ifndef HSTU_ATTN_H
+#define HSTU_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { HSTU_BF16 = 0, HSTU_FP32 = 1 } hstu_dtype_t;
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID = -1,     /* bad argument (null, misaligned, out of range) */
+  HSTU_ERR_UNSUPPORTED = -2, /* valid but not supported (e.g. D = 96, nfunc too large) */
+  HSTU_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+  HSTU_ERR_DEVICE = -4,      /* a HIP runtime call failed */
+  HSTU_ERR_INPUT = -5        /* hstu_attn_check_inputs found malformed device data */
+} hstu_status_t;
+
+/* Largest nfunc accepted (odd).  The reference wheel fixed nfunc at build time
+ * and a proposed query op reported it (PR #670 review thread); here nfunc is a
+ * runtime argument up to this bound. */
+int hstu_max_nfunc(void);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* hstu_last_error(void);
+
+/* Bytes of device workspace a call needs (fwd: is_bwd = 0, bwd: 1) for these
+ * sizes; targets_only != 0 for the targets-only mode.  Returns 0 for sizes the
+ * library does not support (the entry point then reports why).  The workspace
+ * is scratch: its contents need not be preserved between calls. */
+size_t hstu_attn_workspace_size(int is_bwd, int dtype, int64_t B, int64_t total, int H, int D,
+                                int nfunc, int targets_only);
+
+/* Forward: writes o ([total,H,D], or [B,H,D] when target_rows != NULL).
+ * q has the shape of o; k, v are [total,H,D]. */
+int hstu_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o,
+                  const int64_t* seq_offsets, int64_t B, int64_t total, int H, int D,
+                  const int32_t* func, int nfunc, float alpha, int64_t max_len,
+                  const int32_t* target_rows, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* Backward: from dout (shape of o) writes dq (shape of q) and dk, dv
+ * ([total,H,D]).  dk and dv are deterministic (bitwise repeatable); so is dq. */
+int hstu_attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* dout,
+                  void* dq, void* dk, void* dv, const int64_t* seq_offsets, int64_t B,
+                  int64_t total, int H, int D, const int32_t* func, int nfunc, float alpha,
+                  int64_t max_len, const int32_t* target_rows, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Visible-column count |V_i| of every query row: counts is int32 [total]
+ * (or [B] with target_rows), total_pairs a device int64 receiving their sum.
+ * Either output may be NULL.  Integer work: exact. */
+int hstu_attn_visible_counts(const int64_t* seq_offsets, int64_t B, int64_t total,
+                             const int32_t* func, int nfunc, const int32_t* target_rows,
+                             int32_t* counts, int64_t* total_pairs, void* stream);
+
+/* Validates device-resident inputs: seq_offsets[0] == 0, nondecreasing,
+ * seq_offsets[B] == total, and (if given) 0 <= target_rows[b] < L_b for every
+ * non-empty sequence.  Needs hstu_attn_workspace_size(0, ...) bytes of
+ * workspace.  Synchronizes `stream`; returns HSTU_OK or HSTU_ERR_INPUT. */
+int hstu_attn_check_inputs(const int64_t* seq_offsets, int64_t B, int64_t total,
+                           const int32_t* target_rows, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_ATTN_H */

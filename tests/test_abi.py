@@ -1,0 +1,117 @@
+"""C ABI of libhstu_attn.so on the CPU: the library loads, exports every entry
+point include/hstu_attn.h declares, and rejects bad arguments on the host before
+any device work (no kernel is launched by these tests)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import hstu_jagged_masked_amd as hj
+
+    if not os.path.exists(hj.LIBRARY):
+        from hstu_jagged_masked_amd import build
+
+        build.build()
+    return hj.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(hstu_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == sorted(["hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size",
+                            "hstu_attn_fwd", "hstu_attn_bwd", "hstu_attn_visible_counts",
+                            "hstu_attn_check_inputs"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_binding_names_match_header():
+    import hstu_jagged_masked_amd as hj
+
+    assert sorted(hj.EXPORTED) == declared_functions()
+
+
+def test_max_nfunc(lib):
+    assert lib.hstu_max_nfunc() == 9
+
+
+def test_workspace_size(lib):
+    ws = lib.hstu_attn_workspace_size
+    assert ws(0, 0, 32, 32 * 1024, 4, 128, 5, 0) > 0
+    assert ws(1, 0, 32, 32 * 1024, 4, 128, 5, 0) >= ws(0, 0, 32, 32 * 1024, 4, 128, 5, 0)
+    assert ws(0, 0, 32, 32 * 1024, 4, 128, 5, 1) > ws(0, 0, 32, 32 * 1024, 4, 128, 5, 0)
+    assert ws(0, 0, 0, 10, 4, 128, 5, 0) == 0      # B < 1
+    assert ws(0, 0, 2, 10, 4, 128, 11, 0) == 0     # nfunc too large
+    assert ws(0, 0, 2, -1, 4, 128, 5, 0) == 0      # negative total
+
+
+FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation
+
+
+def _fwd(lib, dtype=0, B=2, total=10, H=2, D=128, nfunc=5, alpha=0.1, max_len=8, ws_bytes=1 << 20,
+         q=FAKE, off=FAKE, func=FAKE, tr=None, ws=FAKE):
+    P = ctypes.c_void_p
+    return lib.hstu_attn_fwd(dtype, P(q), P(FAKE), P(FAKE), P(FAKE), P(off), B, total, H, D,
+                             P(func), nfunc, alpha, max_len, None if tr is None else P(tr),
+                             P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    (dict(dtype=7), -1, "dtype"),
+    (dict(B=0), -1, "B must be"),
+    (dict(D=96), -2, "D must be"),
+    (dict(H=0), -1, "H must be"),
+    (dict(H=256), -2, "H must be"),
+    (dict(nfunc=4), -1, "odd"),
+    (dict(nfunc=11), -2, "nfunc must be <="),
+    (dict(alpha=math.nan), -1, "alpha"),
+    (dict(alpha=math.inf), -1, "alpha"),
+    (dict(max_len=0), -1, "max_len"),
+    (dict(off=0), -1, "seq_offsets is NULL"),
+    (dict(func=0), -1, "func is NULL"),
+    (dict(q=0), -1, "q is NULL"),
+    (dict(q=FAKE + 2), -1, "aligned"),
+    (dict(off=FAKE + 8), -1, "aligned"),
+    (dict(ws_bytes=16), -3, "workspace"),
+    (dict(ws=0), -3, "workspace"),
+    (dict(total=-5), -1, "total"),
+])
+def test_fwd_rejects_bad_arguments(lib, kwargs, status, needle):
+    assert _fwd(lib, **kwargs) == status
+    assert needle in lib.hstu_last_error().decode()
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    st = lib.hstu_attn_bwd(0, f, f, f, f, f, f, None, f, 2, 10, 2, 128, f, 5, 0.1, 8, None, f,
+                           1 << 20, None)
+    assert st == -1 and "dv is NULL" in lib.hstu_last_error().decode()
+    st = lib.hstu_attn_bwd(0, f, f, f, f, f, f, f, f, 2, 10, 2, 128, f, 3, 0.1, 0, None, f,
+                           1 << 20, None)
+    assert st == -1 and "max_len" in lib.hstu_last_error().decode()
+
+
+def test_counts_and_check_reject_bad_arguments(lib):
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    assert lib.hstu_attn_visible_counts(f, 0, 10, f, 5, None, f, f, None) == -1
+    assert lib.hstu_attn_visible_counts(f, 2, 10, f, 2, None, f, f, None) == -1
+    assert lib.hstu_attn_visible_counts(None, 2, 10, f, 5, None, f, f, None) == -1
+    assert lib.hstu_attn_check_inputs(f, 2, 10, None, f, 8, None) == -3
+    assert lib.hstu_attn_check_inputs(None, 2, 10, None, f, 1 << 20, None) == -1

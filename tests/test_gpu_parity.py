@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the fp64 oracle.
+
+Tolerances: fp32 inputs -> max|gpu - oracle| / max|oracle| <= 1e-5 per tensor;
+bf16 inputs -> max|gpu - oracle| <= 2e-2 and, additionally, max|err| / max|ref|
+<= 2e-2 per tensor (outputs of unit-scale inputs are ~1e-2 in size, so the
+absolute bound alone would be weak).  The absolute bound is stated for outputs of
+unit scale; cases whose outputs exceed 1 in magnitude (a tiny max_len) apply it
+to err / max(1, max|ref|).  Visible counts are compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def hj():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import hstu_jagged_masked_amd as hj
+
+    hj.library()  # raises if the HIP library was not built
+    return hj
+
+
+DEV = "cuda"
+
+
+def make_inputs(lengths, H, D, dtype, seed, targets=None):
+    lengths = np.asarray(lengths, dtype=np.int64)
+    T = int(lengths.sum())
+    rows_q = len(lengths) if targets is not None else T
+    out = {}
+    for name, shape, s in (("q", (rows_q, H, D), seed), ("k", (T, H, D), seed + 1),
+                           ("v", (T, H, D), seed + 2), ("do", (rows_q, H, D), seed + 3)):
+        if dtype == "bf16":
+            bits, vals = wl.normal_bf16(shape, s)
+            t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+            out[name] = (t, vals.astype(np.float64))
+        else:
+            vals = wl.normal_f32(shape, s)
+            out[name] = (torch.from_numpy(vals).to(DEV), vals.astype(np.float64))
+    return out
+
+
+def rel_err(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    if want.size == 0:
+        return 0.0, 0.0
+    err = float(np.max(np.abs(got - want)))
+    scale = float(np.max(np.abs(want)))
+    return err, err / scale if scale > 0 else err
+
+
+def assert_parity(name, got_t, want, dtype):
+    got = got_t.float().cpu().numpy().astype(np.float64)
+    assert got.shape == want.shape, f"{name}: shape {got.shape} vs {want.shape}"
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    err, rel = rel_err(got, want)
+    if dtype == "fp32":
+        assert rel <= 1e-5, f"{name}: rel err {rel:.3e} (abs {err:.3e})"
+    else:
+        scale = float(np.max(np.abs(want))) if want.size else 0.0
+        assert err <= 2e-2 * max(1.0, scale), f"{name}: max abs err {err:.3e}"
+        assert rel <= 2e-2, f"{name}: rel err {rel:.3e} (abs {err:.3e})"
+    return err, rel
+
+
+def run_case(hj, lengths, H, D, dtype, func, alpha, max_len, seed=7, targets=None, bwd=True):
+    lengths = np.asarray(lengths, dtype=np.int64)
+    off = wl.offsets_from_lengths(lengths)
+    inp = make_inputs(lengths, H, D, dtype, seed, targets)
+    off_t = torch.from_numpy(off).to(DEV)
+    func_t = torch.from_numpy(np.ascontiguousarray(func)).to(DEV)
+    tr_t = None if targets is None else torch.from_numpy(np.asarray(targets, np.int32)).to(DEV)
+    (q, qn), (k, kn), (v, vn), (do, don) = inp["q"], inp["k"], inp["v"], inp["do"]
+    o = hj.attn_fwd(q, k, v, off_t, func_t, alpha, max_len, tr_t)
+    torch.cuda.synchronize()
+    want_o = oracle.fwd(qn, kn, vn, off, func, alpha, max_len, targets)
+    res = {"o": assert_parity("o", o, want_o, dtype)}
+    if bwd:
+        dq, dk, dv = hj.attn_bwd(q, k, v, do, off_t, func_t, alpha, max_len, tr_t)
+        torch.cuda.synchronize()
+        wq, wk, wv = oracle.bwd(qn, kn, vn, don, off, func, alpha, max_len, targets)
+        res["dq"] = assert_parity("dq", dq, wq, dtype)
+        res["dk"] = assert_parity("dk", dk, wk, dtype)
+        res["dv"] = assert_parity("dv", dv, wv, dtype)
+    counts, total = hj.visible_counts(off_t, func_t, int(off[-1]), tr_t)
+    want_c, want_total = oracle.visible_counts(off, func, targets)
+    assert np.array_equal(counts.cpu().numpy(), want_c), "visible counts differ"
+    assert int(total.item()) == want_total, "total pairs differ"
+    return res
+
+
+# --- the small fp32 configuration: B=2 lengths 37 and 64, H=2, D=32 --------
+
+
+def test_tiny_fp32_causal(hj):
+    cfg = wl.workload("tiny_fp32")
+    ls = cfg["lengths"]
+    run_case(hj, ls, cfg["H"], cfg["D"], "fp32", cfg["func"](ls), cfg["alpha"], cfg["max_len"],
+             seed=1)
+
+
+def test_tiny_fp32_targets_only(hj):
+    cfg = wl.workload("tiny_fp32")
+    ls = cfg["lengths"]
+    run_case(hj, ls, cfg["H"], cfg["D"], "fp32", cfg["func"](ls), cfg["alpha"], cfg["max_len"],
+             seed=1, targets=wl.targets_last(ls))
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_fp32_random_func(hj, D):
+    ls = np.array([5, 0, 40, 1, 70])
+    run_case(hj, ls, 3, D, "fp32", wl.func_random(ls, 7, 99, spread=6), 0.2, 70, seed=3)
+
+
+# --- bf16 ----------------------------------------------------------------
+
+RAGGED = [1, 37, 64, 130, 257, 300, 0, 129]
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_bf16_causal_ragged(hj, D):
+    ls = np.array(RAGGED)
+    run_case(hj, ls, 2, D, "bf16", wl.func_causal(ls, 5), 1 / np.sqrt(D), int(ls.max()), seed=11)
+
+
+def test_bf16_sla_nfunc5_equals_nfunc3(hj):
+    ls = np.array([600, 333, 1000])
+    H, D = 2, 128
+    r5 = run_case(hj, ls, H, D, "bf16", wl.func_sla(ls, 256, 32, 5), 1 / np.sqrt(D), 1000,
+                  seed=12)
+    r3 = run_case(hj, ls, H, D, "bf16", wl.func_sla(ls, 256, 32, 3), 1 / np.sqrt(D), 1000,
+                  seed=12)
+    for key in r5:
+        assert r5[key] == r3[key], f"{key}: nfunc=5 and nfunc=3 differ"
+
+
+def test_bf16_sla_padded_bitwise(hj):
+    """Padding empty intervals onto the 2-interval func gives identical bits."""
+    ls = np.array([700, 128, 900])
+    H, D = 2, 128
+    off = wl.offsets_from_lengths(ls)
+    inp = make_inputs(ls, H, D, "bf16", 13)
+    off_t = torch.from_numpy(off).to(DEV)
+    outs = []
+    for nf in (3, 5, 9):
+        f = torch.from_numpy(wl.func_sla(ls, 256, 32, nf)).to(DEV)
+        o = hj.attn_fwd(inp["q"][0], inp["k"][0], inp["v"][0], off_t, f, 0.09, 900)
+        g = hj.attn_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], off_t, f, 0.09, 900)
+        outs.append((o,) + tuple(g))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    for a, b in zip(outs[0], outs[2]):
+        assert torch.equal(a, b)
+
+
+def test_bf16_three_interval(hj):
+    ls = np.array([300, 520, 270, 100])
+    run_case(hj, ls, 2, 128, "bf16", wl.func_three_interval(ls, 32, 8, 5), 1 / np.sqrt(128),
+             520, seed=14)
+
+
+@pytest.mark.parametrize("nfunc", [1, 3, 5, 9])
+def test_bf16_random_func(hj, nfunc):
+    ls = np.array([5, 0, 77, 200, 64, 65])
+    run_case(hj, ls, 2, 128, "bf16", wl.func_random(ls, nfunc, 100 + nfunc, spread=20), 0.1, 200,
+             seed=15)
+
+
+def test_bf16_targets_only(hj):
+    ls = np.array([300, 1, 129, 700, 0, 64])
+    tr = np.array([299, 0, 5, 699, 0, 63], dtype=np.int32)
+    run_case(hj, ls, 4, 128, "bf16", wl.func_causal(ls, 5), 1 / np.sqrt(128), 700, seed=16,
+             targets=tr)
+
+
+def test_bf16_targets_only_sla(hj):
+    ls = np.array([1000, 513, 64])
+    run_case(hj, ls, 2, 128, "bf16", wl.func_sla(ls, 256, 32, 5), 1 / np.sqrt(128), 1000,
+             seed=17, targets=wl.targets_last(ls))
+
+
+def test_empty_and_single_rows(hj):
+    run_case(hj, np.array([1]), 1, 128, "bf16", wl.func_causal([1], 5), 0.5, 1, seed=18)
+    run_case(hj, np.array([0, 3, 0]), 1, 128, "bf16", wl.func_causal([0, 3, 0], 5), 0.5, 3,
+             seed=19)
+    run_case(hj, np.array([0, 0]), 2, 64, "bf16", np.zeros((5, 0), np.int32), 0.5, 1, seed=20)
+
+
+def test_unseen_key_rows_get_zero_grad(hj):
+    """Key rows no query sees must come back with dK = dV = 0 exactly: every
+    row sees [0, min(i+1, 50)), so local columns >= 50 are never seen."""
+    ls = np.array([200, 150, 30])
+    local = wl.local_rows(ls)
+    f = np.minimum(local + 1, 50).astype(np.int32)[None, :]
+    H, D = 2, 128
+    inp = make_inputs(ls, H, D, "bf16", 21)
+    off_t = torch.from_numpy(wl.offsets_from_lengths(ls)).to(DEV)
+    dq, dk, dv = hj.attn_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], off_t,
+                             torch.from_numpy(f).to(DEV), 0.1, 200)
+    unseen = torch.from_numpy(local >= 50).to(DEV)
+    seen = ~unseen
+    assert int(unseen.sum()) == 150 + 100
+    assert torch.all(dk[unseen] == 0) and torch.all(dv[unseen] == 0)
+    assert torch.any(dk[seen] != 0) and torch.any(dv[seen] != 0)
+
+
+def test_dk_dv_bitwise_repeatable(hj):
+    ls = np.array([700, 300, 1000, 64])
+    H, D = 2, 128
+    off = wl.offsets_from_lengths(ls)
+    inp = make_inputs(ls, H, D, "bf16", 22)
+    off_t = torch.from_numpy(off).to(DEV)
+    ft = torch.from_numpy(wl.func_causal(ls, 5)).to(DEV)
+    ref = hj.attn_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], off_t, ft, 0.09, 1000)
+    for _ in range(10):
+        g = hj.attn_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], off_t, ft, 0.09,
+                        1000)
+        for a, b in zip(ref, g):
+            assert torch.equal(a, b)
+
+
+def test_check_inputs(hj):
+    off = torch.tensor([0, 3, 7], dtype=torch.int64, device=DEV)
+    hj.check_inputs(off, 7)
+    hj.check_inputs(off, 7, torch.tensor([2, 3], dtype=torch.int32, device=DEV))
+    with pytest.raises(hj.HstuError, match="seq_offsets\\[B\\] != total"):
+        hj.check_inputs(off, 8)
+    with pytest.raises(hj.HstuError, match="decreasing"):
+        hj.check_inputs(torch.tensor([0, 5, 3, 7], dtype=torch.int64, device=DEV), 7)
+    with pytest.raises(hj.HstuError, match="target row"):
+        hj.check_inputs(off, 7, torch.tensor([3, 0], dtype=torch.int32, device=DEV))
+
+
+def test_malformed_offsets_stay_in_bounds(hj):
+    """Garbage offsets give garbage but no fault: kernels clamp them."""
+    ls = np.array([100, 50])
+    inp = make_inputs(ls, 2, 128, "bf16", 23)
+    bad = torch.tensor([5, 400, -7], dtype=torch.int64, device=DEV)
+    ft = torch.from_numpy(wl.func_causal(ls, 5)).to(DEV)
+    o = hj.attn_fwd(inp["q"][0], inp["k"][0], inp["v"][0], bad, ft, 0.1, 100)
+    g = hj.attn_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], bad, ft, 0.1, 100)
+    torch.cuda.synchronize()
+    assert o.shape == inp["q"][0].shape and g[0].shape == o.shape
