@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark: HSTU jagged masked attention, forward + backward, on one MI355X.
+
+Workload (the production HSTU layer shape): B = 1024 sequences of 2663 rows
+(2,726,912 tokens), H = 4 heads, D = 128, bf16, causal func encoded with
+nfunc = 5 (two pad intervals), alpha = 1/sqrt(128), max_len = 2663.  Inputs
+are synthetic N(0, 1) drawn on the device with torch's seeded generator and
+are resident in HBM before timing starts.  One step = hstu_attn_fwd followed by
+hstu_attn_bwd over the whole batch.
+
+Reported ("value"): effective TFLOP/s = 14 * D * H * sum_i |V_i| / step time,
+counting 4*D (forward) + 10*D (backward) flops per visible (query, key) pair and
+head, over unmasked pairs only.  Also reported: the targets-only mode (one
+candidate row per sequence against full-length K/V), per-kernel times measured
+with HIP events on the launch stream during the timed steps, the roofline of
+the dominant kernel, and the fp64 CPU oracle's rate on a sample of sequences.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "HSTU attn fwd+bwd ms + effective TFLOP/s (% bf16 MFMA peak), B=1024 L=2663"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# algorithmic flops per visible pair and head, as multiples of D
+KERNEL_FLOPS_PER_PAIR = {"k_fwd_bf16": 4, "k_bwd_kv": 8, "k_bwd_q": 2}
+KERNEL_SOURCES = {"k_fwd_bf16": ["fwd.hip"], "k_bwd_kv": ["bwd.hip"], "k_bwd_q": ["bwd.hip"],
+                  "k_targets_fwd": ["targets.hip"], "k_targets_bwd": ["targets.hip"]}
+COMMON_SOURCES = ["common.h", "tiles.h"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hstu_jagged_masked_amd", "csrc")
+    for name in KERNEL_SOURCES.get(kernel, []) + COMMON_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current source of that kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(kernel)
+    if not rec or rec.get("source_sha256") != source_digest(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def make_inputs(cfg, device, targets=False):
+    import torch
+
+    lengths = cfg["lengths"]
+    off = wl.offsets_from_lengths(lengths)
+    T = int(off[-1])
+    B, H, D = len(lengths), cfg["H"], cfg["D"]
+    seed = cfg["seed"]
+    rows_q = B if targets else T
+    dt = torch.bfloat16
+    t = {
+        "off": torch.from_numpy(off).to(device),
+        "func": torch.from_numpy(cfg["func"](lengths, cfg["nfunc"])).to(device),
+        "k": wl.normal_device((T, H, D), seed * 10 + 1, dt, device),
+        "v": wl.normal_device((T, H, D), seed * 10 + 2, dt, device),
+        "q": wl.normal_device((rows_q, H, D), seed * 10 + (5 if targets else 0), dt, device),
+        "do": wl.normal_device((rows_q, H, D), seed * 10 + (6 if targets else 3), dt, device),
+    }
+    if targets:
+        t["tr"] = torch.from_numpy(wl.targets_last(lengths)).to(device)
+    return t, off
+
+
+def run_steps(hj, t, cfg, n, targets=False):
+    tr = t.get("tr") if targets else None
+    for _ in range(n):
+        hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], t["func"], cfg["alpha"], cfg["max_len"], tr)
+        hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], t["func"], cfg["alpha"],
+                    cfg["max_len"], tr)
+
+
+def timed(hj, torch, t, cfg, steps, targets=False):
+    torch.cuda.synchronize()
+    hj.profile_reset()
+    hj.profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    run_steps(hj, t, cfg, steps, targets)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    hj.profile_enable(False)
+    prof = hj.profile_read()
+    return e0.elapsed_time(e1) / steps, wall, prof
+
+
+def cpu_baseline(cfg, t, off, nseq):
+    """The fp64 oracle on the first `nseq` sequences (fwd + bwd), host cores."""
+    import oracle
+
+    rows, sub_off = oracle.subset(off, list(range(nseq)))
+    lo, hi = int(rows[0]), int(rows[-1]) + 1
+    to64 = lambda x: x[lo:hi].float().cpu().numpy().astype(np.float64)  # noqa: E731
+    q, k, v, do = (to64(t[n]) for n in ("q", "k", "v", "do"))
+    func = t["func"][:, lo:hi].cpu().numpy()
+    orc = oracle.default()
+    counts, pairs = orc.visible_counts(sub_off, func)
+    t0 = time.perf_counter()
+    orc.fwd(q, k, v, sub_off, func, cfg["alpha"], cfg["max_len"])
+    orc.bwd(q, k, v, do, sub_off, func, cfg["alpha"], cfg["max_len"])
+    dt = time.perf_counter() - t0
+    flops = 14.0 * cfg["D"] * cfg["H"] * pairs
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, nseq * cfg["H"]),
+            "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd on {nseq} of {len(cfg['lengths'])} sequences "
+                      f"(L={int(cfg['lengths'][0])}, all {cfg['H']} heads), {dt:.2f} s, "
+                      f"effective flops 14*D per visible pair"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="hstu_2663", choices=wl.WORKLOADS)
+    ap.add_argument("--targets-steps", type=int, default=20)
+    ap.add_argument("--cpu-seqs", type=int, default=8,
+                    help="sequences in the CPU oracle sample (0 disables it)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "the operator has no cross-GPU step; see the sharding notes in DESIGN.md",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import hstu_jagged_masked_amd as hj
+
+    hj.library()
+    device = torch.device("cuda:0")
+    cfg = wl.workload(args.workload)
+    if cfg["dtype"] != "bf16":
+        raise SystemExit("bench.py times the bf16 workloads")
+    H, D = cfg["H"], cfg["D"]
+    log(f"[bench] workload {args.workload}: B={len(cfg['lengths'])} H={H} D={D}")
+    t, off = make_inputs(cfg, device)
+    _, pairs_t = hj.visible_counts(t["off"], t["func"], int(off[-1]))
+    pairs = int(pairs_t.item())
+    log(f"[bench] visible pairs per head: {pairs}")
+
+    run_steps(hj, t, cfg, args.warmup)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    ms, wall, prof = timed(hj, torch, t, cfg, args.steps)
+    log(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step")
+    flops_eff = 14.0 * D * H * pairs
+    value = flops_eff / (ms * 1e-3) / 1e12
+
+    kernels = {}
+    for name, (count, total_ms) in sorted(prof.items()):
+        per = total_ms / max(count, 1)
+        rec = {"launches": count, "avg_ms": round(per, 4), "ms_per_step": round(total_ms / args.steps, 4)}
+        if name in KERNEL_FLOPS_PER_PAIR:
+            fl = KERNEL_FLOPS_PER_PAIR[name] * D * H * pairs
+            rec["algorithmic_tflop_per_launch"] = round(fl / 1e12, 4)
+            rec["tflops"] = round(fl / (per * 1e-3) / 1e12, 1)
+        kernels[name] = rec
+    dom = max((k for k in kernels if k in KERNEL_FLOPS_PER_PAIR),
+              key=lambda k: kernels[k]["ms_per_step"])
+    ach = kernels[dom]["tflops"]
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom)}
+
+    # targets-only mode on the same K/V
+    tt, _ = make_inputs(cfg, device, targets=True)
+    tt["k"], tt["v"] = t["k"], t["v"]
+    run_steps(hj, tt, cfg, 2, targets=True)
+    t_ms, _, t_prof = timed(hj, torch, tt, cfg, args.targets_steps, targets=True)
+    log(f"[bench] targets-only: {t_ms:.3f} ms/step")
+    T = int(off[-1])
+    # fwd streams K, V; bwd streams K, V in and dK, dV out (bf16)
+    t_bytes = 6.0 * T * H * D * 2
+    targets = {"ms_per_step": round(t_ms, 4), "speedup_vs_full": round(ms / t_ms, 2),
+               "algorithmic_gb": round(t_bytes / 1e9, 3),
+               "gbs": round(t_bytes / (t_ms * 1e-3) / 1e9, 1),
+               "frac_hbm_peak": round(t_bytes / (t_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+               "kernels": {k: {"launches": c, "avg_ms": round(m / max(c, 1), 4)}
+                           for k, (c, m) in sorted(t_prof.items())}}
+    del tt
+
+    cpu = None
+    if args.cpu_seqs > 0:
+        log(f"[bench] cpu oracle baseline on {args.cpu_seqs} sequences ...")
+        cpu = cpu_baseline(cfg, t, off, args.cpu_seqs)
+        log(f"[bench] cpu oracle: {cpu['value']:.6f} TFLOP/s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": len(cfg["lengths"]),
+                   "seq_len": int(cfg["lengths"].max()), "tokens": T, "heads": H, "head_dim": D,
+                   "nfunc": cfg["nfunc"], "mask": "causal" if "hstu" in args.workload else
+                   args.workload, "visible_pairs_per_head": pairs},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "targets_only": targets,
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

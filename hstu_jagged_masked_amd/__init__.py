@@ -70,12 +70,19 @@ def library() -> ctypes.CDLL:
     lib.hstu_attn_visible_counts.restype = i32
     lib.hstu_attn_check_inputs.argtypes = [P, i64, i64, P, P, sz, P]
     lib.hstu_attn_check_inputs.restype = i32
+    lib.hstu_profile_enable.argtypes = [i32]
+    lib.hstu_profile_enable.restype = i32
+    lib.hstu_profile_read.argtypes = [ctypes.c_char_p, sz]
+    lib.hstu_profile_read.restype = sz
+    lib.hstu_profile_reset.argtypes = []
+    lib.hstu_profile_reset.restype = None
     _lib = lib
     return lib
 
 
 EXPORTED = ("hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size", "hstu_attn_fwd",
-            "hstu_attn_bwd", "hstu_attn_visible_counts", "hstu_attn_check_inputs")
+            "hstu_attn_bwd", "hstu_attn_visible_counts", "hstu_attn_check_inputs",
+            "hstu_profile_enable", "hstu_profile_read", "hstu_profile_reset")
 
 
 def _check(status: int):
@@ -188,6 +195,28 @@ def check_inputs(seq_offsets, total, target_rows=None):
     ws = _workspace(workspace_size(0, HSTU_BF16, B, total, 1, 128, 1, 0), seq_offsets.device)
     _check(library().hstu_attn_check_inputs(_ptr(seq_offsets), B, int(total), _ptr(target_rows),
                                             _ptr(ws), ws.numel(), _stream(seq_offsets.device)))
+
+
+def profile_enable(on: bool = True) -> bool:
+    """Turn per-kernel HIP-event timing on or off; returns the previous state."""
+    return bool(library().hstu_profile_enable(1 if on else 0))
+
+
+def profile_reset() -> None:
+    library().hstu_profile_reset()
+
+
+def profile_read() -> dict:
+    """{kernel_name: (launches, total_ms)} accumulated since the last reset."""
+    lib = library()
+    need = lib.hstu_profile_read(None, 0)
+    buf = ctypes.create_string_buffer(int(need) + 64)
+    lib.hstu_profile_read(buf, len(buf))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, count, ms = line.split()
+        out[name] = (int(count), float(ms))
+    return out
 
 
 class HstuAttention(torch.autograd.Function):

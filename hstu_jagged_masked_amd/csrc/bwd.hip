@@ -343,6 +343,7 @@ hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const vo
                            float inv_max_len, hipStream_t stream) {
   const float scale = alpha * inv_max_len;
   if (Ukv.cap > 0) {
+    ProfScope ps(stream, "k_bwd_kv");
     hipLaunchKernelGGL(k_bwd_kv, dim3(Ukv.cap), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout),
@@ -352,6 +353,7 @@ hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const vo
     if (e != hipSuccess) return e;
   }
   if (Uq.cap > 0) {
+    ProfScope ps(stream, "k_bwd_q");
     hipLaunchKernelGGL(k_bwd_q, dim3(Uq.cap), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout),

@@ -84,6 +84,23 @@ bool plan_workspace(Plan& plan, int is_bwd, int dtype, int64_t B, int64_t total,
 Prep prep_view(const Plan& plan, void* ws, int B, int64_t total);
 
 // ---------------------------------------------------------------------------
+// per-kernel timing: while profiling is on (hstu_profile_enable), a ProfScope
+// records a HIP event before and after the kernel it wraps, on its stream.
+// ---------------------------------------------------------------------------
+class ProfScope {
+ public:
+  ProfScope(hipStream_t stream, const char* name);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  hipStream_t stream_;
+  const char* name_;
+  hipEvent_t start_ = nullptr;
+};
+
+// ---------------------------------------------------------------------------
 // launchers (each returns a hipError_t from the launch)
 // ---------------------------------------------------------------------------
 hipError_t launch_prep(const Prep& P, const int64_t* seq_offsets, const int32_t* target_rows,

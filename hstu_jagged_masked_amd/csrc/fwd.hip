@@ -196,6 +196,7 @@ hipError_t launch_mfma_fwd(const void* q, const void* k, const void* v, void* o,
                            const Units& U, int H, const int32_t* func, int nfunc, float alpha,
                            float inv_max_len, hipStream_t stream) {
   if (U.cap == 0) return hipSuccess;
+  ProfScope ps(stream, "k_fwd_bf16");
   hipLaunchKernelGGL(k_fwd_bf16, dim3(U.cap), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), P, U.list,

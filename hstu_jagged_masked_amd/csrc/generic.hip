@@ -199,6 +199,7 @@ hipError_t fwd_impl(const void* q, const void* k, const void* v, void* o, const 
   const int64_t rows = target_rows ? P.B : P.total;
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)((rows + 63) / 64), H);
+  ProfScope ps(stream, "k_generic_fwd");
   hipLaunchKernelGGL((k_fwd_rows<T, D>), grid, dim3(64), 0, stream, (const T*)q, (const T*)k,
                      (const T*)v, (T*)o, P, H, func, nfunc, alpha, inv_max_len, target_rows);
   return hipGetLastError();
@@ -212,6 +213,7 @@ hipError_t bwd_impl(const void* q, const void* k, const void* v, const void* dou
   const int64_t rows = target_rows ? P.B : P.total;
   if (rows > 0) {
     dim3 grid((unsigned)((rows + 63) / 64), H);
+    ProfScope ps(stream, "k_generic_bwd_rows");
     hipLaunchKernelGGL((k_bwd_rows<T, D>), grid, dim3(64), 0, stream, (const T*)q, (const T*)k,
                        (const T*)v, (const T*)dout, (T*)dq, P, H, func, nfunc, alpha,
                        inv_max_len, target_rows);
@@ -220,6 +222,7 @@ hipError_t bwd_impl(const void* q, const void* k, const void* v, const void* dou
   }
   if (P.total > 0) {
     dim3 grid((unsigned)((P.total + 63) / 64), H, D / 32);
+    ProfScope ps(stream, "k_generic_bwd_cols");
     hipLaunchKernelGGL((k_bwd_cols<T, D>), grid, dim3(64), 0, stream, (const T*)q, (const T*)k,
                        (const T*)v, (const T*)dout, (T*)dk, (T*)dv, P, H, func, nfunc, alpha,
                        inv_max_len, target_rows);

@@ -276,10 +276,15 @@ __global__ void k_visible_counts(const int64_t* __restrict__ off, int B, int64_t
 
 hipError_t launch_prep(const Prep& P, const int64_t* seq_offsets, const int32_t* target_rows,
                        const int32_t* func, int nfunc, hipStream_t stream) {
-  hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, stream, P, seq_offsets, target_rows);
+  {
+    ProfScope ps(stream, "k_prep");
+    hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, stream, P, seq_offsets,
+                       target_rows);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || func == nullptr) return e;
   if (P.nrb_cap > 0) {
+    ProfScope ps(stream, "k_envelopes");
     hipLaunchKernelGGL(k_envelopes, dim3(P.nrb_cap), dim3(64), 0, stream, P, func, nfunc);
     e = hipGetLastError();
   }
@@ -290,6 +295,7 @@ hipError_t launch_units(const Prep& P, const Units& U, int tile, int descending,
                         int count_slot, hipStream_t stream) {
   const int threads = 256;
   const int blocks = (U.cap + threads - 1) / threads;
+  ProfScope ps(stream, "k_units");
   hipLaunchKernelGGL(k_units, dim3(blocks > 0 ? blocks : 1), dim3(threads), 0, stream, P, U, tile,
                      descending, H, count_slot);
   return hipGetLastError();
@@ -307,6 +313,7 @@ hipError_t launch_visible_counts(const int64_t* seq_offsets, int B, int64_t tota
   if (n == 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (n + threads - 1) / threads;
+  ProfScope ps(stream, "k_visible_counts");
   hipLaunchKernelGGL(k_visible_counts, dim3((unsigned)blocks), dim3(threads), 0, stream,
                      seq_offsets, B, total, func, nfunc, target_rows, counts,
                      reinterpret_cast<unsigned long long*>(total_pairs));

@@ -257,12 +257,14 @@ hipError_t fwd_impl(const void* q, const void* k, const void* v, void* o, const 
                     const Units& U, int H, const int32_t* func, int nfunc, float alpha,
                     float scale, const int32_t* target_rows, float* partial, hipStream_t stream) {
   if (U.cap > 0) {
+    ProfScope ps(stream, "k_targets_fwd");
     hipLaunchKernelGGL((k_targets_fwd<T, D>), dim3(U.cap), dim3(64 * kWaves), 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, partial, P, U.list,
                        P.flags + kSlotFwdUnits, H, func, nfunc, alpha, target_rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  ProfScope ps(stream, "k_targets_reduce");
   hipLaunchKernelGGL((k_targets_reduce<T, D>), dim3(P.B, H), dim3(D), 0, stream,
                      (const float*)partial, (T*)o, P, H, scale);
   return hipGetLastError();
@@ -274,6 +276,7 @@ hipError_t bwd_impl(const void* q, const void* k, const void* v, const void* dou
                     int nfunc, float alpha, float scale, const int32_t* target_rows,
                     float* partial, hipStream_t stream) {
   if (U.cap > 0) {
+    ProfScope ps(stream, "k_targets_bwd");
     hipLaunchKernelGGL((k_targets_bwd<T, D>), dim3(U.cap), dim3(64 * kWaves), 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)dout, (T*)dk, (T*)dv,
                        partial, P, U.list, P.flags + kSlotFwdUnits, H, func, nfunc, alpha, scale,
@@ -281,6 +284,7 @@ hipError_t bwd_impl(const void* q, const void* k, const void* v, const void* dou
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  ProfScope ps(stream, "k_targets_reduce");
   hipLaunchKernelGGL((k_targets_reduce<T, D>), dim3(P.B, H), dim3(D), 0, stream,
                      (const float*)partial, (T*)dq, P, H, scale);
   return hipGetLastError();

@@ -122,6 +122,17 @@ int hstu_attn_check_inputs(const int64_t* seq_offsets, int64_t B, int64_t total,
                            const int32_t* target_rows, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Per-kernel timing (a profiling aid, not part of the operator).  While
+ * enabled, every kernel an entry point enqueues is bracketed by a HIP event
+ * pair recorded on the same stream.  hstu_profile_enable returns the previous
+ * state.  hstu_profile_read waits for the recorded events, folds them into
+ * per-kernel totals and writes lines "kernel_name count total_ms" into buf
+ * (NUL-terminated, truncated to len); it returns the size needed including
+ * the NUL.  hstu_profile_reset drops all totals. */
+int hstu_profile_enable(int on);
+size_t hstu_profile_read(char* buf, size_t len);
+void hstu_profile_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

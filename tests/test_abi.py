@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size",
                             "hstu_attn_fwd", "hstu_attn_bwd", "hstu_attn_visible_counts",
-                            "hstu_attn_check_inputs"])
+                            "hstu_attn_check_inputs", "hstu_profile_enable",
+                            "hstu_profile_read", "hstu_profile_reset"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -115,3 +116,12 @@ def test_counts_and_check_reject_bad_arguments(lib):
     assert lib.hstu_attn_visible_counts(None, 2, 10, f, 5, None, f, f, None) == -1
     assert lib.hstu_attn_check_inputs(f, 2, 10, None, f, 8, None) == -3
     assert lib.hstu_attn_check_inputs(None, 2, 10, None, f, 1 << 20, None) == -1
+
+
+def test_profile_toggle_without_device_work(lib):
+    import hstu_jagged_masked_amd as hj
+
+    assert hj.profile_enable(True) is False
+    assert hj.profile_enable(False) is True
+    hj.profile_reset()
+    assert hj.profile_read() == {}
