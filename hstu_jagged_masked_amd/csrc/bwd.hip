@@ -23,6 +23,8 @@
 //               S^T = K Q^T, dS^T = V dO^T      (B = Q, dO registers)
 //               p in registers
 //               dQ^T += K^T P^T                 (A = transpose reads of K)
+#include <type_traits>
+
 #include "common.h"
 #include "tiles.h"
 
@@ -34,7 +36,7 @@ constexpr int kD = 128;
 constexpr int kThreads = 256;
 // k_bwd_kv
 constexpr int kKvBN = 128;         // key rows per workgroup
-constexpr int kKvBM = 64;          // query rows per step (one row block)
+constexpr int kKvBM = 32;          // query rows per step (half a row block)
 constexpr int kQStr = kD + 8;      // LDS row stride of the Q / dO tiles (bf16)
 // k_bwd_q
 constexpr int kQBM = 128;          // query rows per workgroup
@@ -45,7 +47,7 @@ __device__ __forceinline__ bf16x8 concat4(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void k_bwd_kv(
+__global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, Prep P, const int4* __restrict__ units,
@@ -58,9 +60,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_kv(
   const int slot = xcd_slot(blockIdx.x, *unit_count);
   if (slot < 0) return;
   const int4 u = units[slot];
-  const int b = u.x, kt = u.y, h = u.z;
-  const int64_t s = P.so[b];
-  const int L = (int)(P.so[b + 1] - s);
+  const int b = uniform(u.x), kt = uniform(u.y), h = uniform(u.z);
+  const int64_t s = uniform(P.so[b]);
+  const int L = uniform((int)(P.so[b + 1] - s));
   const int c0 = kt * kKvBN;
   const int c1 = min(c0 + kKvBN, L);
   const int tid = threadIdx.x;
@@ -68,6 +70,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_kv(
   const int n = lane & 31, g = lane >> 5;
   const int ni = (nfunc + 1) / 2;
   const int64_t rs = (int64_t)H * kD;
+  const int rs2 = H * kD * 2;
   const float c_exp = -alpha * kLog2e;
 
   // this lane's key column and its K / V rows (B operands: [k = d][n = key])
@@ -90,103 +93,112 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_kv(
     dvacc[mb] = f32x16{};
   }
 
-  // tile loads: rows lrow + 16i of the block, dims lcol..lcol+7
+  // staging: thread loads rows lrow and lrow + 16 of the 32-row step, dims lcol..+7
   const int lrow = tid >> 4, lcol = (tid & 15) * 8;
+  const int voff = lrow * rs2 + lcol * 2;
+  const uint16_t* qh = q + s * rs + (int64_t)h * kD;
+  const uint16_t* gh = dout + s * rs + (int64_t)h * kD;
   // transpose-read base: lane j of 16-lane group G -> row 4*(G/2) + j/4,
   // column (G%2)*16 + 4*(j%4)
   const int grp = lane >> 4, gl = lane & 15;
   const int tr_off = (4 * (grp >> 1) + (gl >> 2)) * kQStr + (grp & 1) * 16 + 4 * (gl & 3);
+  const int rd_off = n * kQStr + g * 8;
 
-  const int nrb = (L + kRB - 1) / kRB;
-  const int4* env = P.env + (int64_t)P.rb_off[b] * ni;
-  for (int rb = 0; rb < nrb; ++rb) {
-    bool live, full;
-    block_vs_cols(env + (int64_t)rb * ni, ni, c0, c1, live, full);
-    if (!live) continue;
-    const int q0 = rb * kRB;
-    // stage the Q and dO rows of this block
+  // one 32-row step: rows q0..q0+31 staged in sQ / sG
+  auto step = [&](auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
+    f32x16 sacc = f32x16{}, dsacc = f32x16{};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = lrow + 16 * i;
-      uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
-      if (q0 + r < L) {
-        a = *reinterpret_cast<const uint4*>(q + (s + q0 + r) * rs + (int64_t)h * kD + lcol);
-        c = *reinterpret_cast<const uint4*>(dout + (s + q0 + r) * rs + (int64_t)h * kD + lcol);
-      }
-      *reinterpret_cast<uint4*>(&sQ[r * kQStr + lcol]) = a;
-      *reinterpret_cast<uint4*>(&sG[r * kQStr + lcol]) = c;
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8*>(&sQ[rd_off + ks * 16]), kf[ks], sacc, 0, 0, 0);
+      dsacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          *reinterpret_cast<const bf16x8*>(&sG[rd_off + ks * 16]), vf[ks], dsacc, 0, 0, 0);
     }
-    if (!full) {
-      // row q0 + lane: visibility of this wave's 32 key columns
-      int lo[kMaxNI], hi[kMaxNI];
-      const int r = q0 + lane;
+    // element r: query row (r/4)*8 + g*4 + r%4 of the step, key column `col`
+    bf16x8 yb[2], pb[2];
 #pragma unroll
-      for (int j = 0; j < kMaxNI; ++j) {
-        lo[j] = L;
-        hi[j] = 0;
-        if (j < ni && r < L) row_interval(func, P.total, s + r, j, L, lo[j], hi[j]);
-      }
-      sMask[wave][lane] = col_mask32(lo, hi, ni, c0 + wave * 32);
-    }
-    __syncthreads();
-
-    // S = Q K^T and dS = dO V^T for the block's two 32-row halves
-    f32x16 sacc[2], dsacc[2];
+    for (int jj = 0; jj < 4; ++jj) {
+      uint4 m4 = make_uint4(0, 0, 0, 0);
+      if constexpr (kMasked) m4 = *reinterpret_cast<const uint4*>(&sMask[wave][jj * 8 + g * 4]);
+      const uint32_t mrow[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
-    for (int mq = 0; mq < 2; ++mq) {
-      sacc[mq] = f32x16{};
-      dsacc[mq] = f32x16{};
-      const uint16_t* qp = &sQ[(mq * 32 + n) * kQStr + g * 8];
-      const uint16_t* gp = &sG[(mq * 32 + n) * kQStr + g * 8];
-#pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) {
-        sacc[mq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(qp + ks * 16), kf[ks], sacc[mq], 0, 0, 0);
-        dsacc[mq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(gp + ks * 16), vf[ks], dsacc[mq], 0, 0, 0);
-      }
-    }
-    // y and p per element: row mq*32 + (r/4)*8 + g*4 + r%4, column `col`
-    bf16x8 yb[4], pb[4];
-#pragma unroll
-    for (int mq = 0; mq < 2; ++mq) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        uint4 m4 = make_uint4(~0u, ~0u, ~0u, ~0u);
-        if (!full) m4 = *reinterpret_cast<const uint4*>(&sMask[wave][mq * 32 + jj * 8 + g * 4]);
-        const uint32_t mrow[4] = {m4.x, m4.y, m4.z, m4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = jj * 4 + i;
-          const float x = sacc[mq][r];
-          const float sg = logistic_scaled(x, c_exp);
-          const float ax = alpha * x;
-          float y = x * sg;
-          float p = dsacc[mq][r] * (sg * (1.0f + ax * (1.0f - sg)));
+      for (int i = 0; i < 4; ++i) {
+        const int r = jj * 4 + i;
+        const float x = sacc[r];
+        const float sg = logistic_scaled(x, c_exp);
+        float y = x * sg;
+        // silu'(alpha x) = sg + alpha * x sg (1 - sg) = sg + alpha * (y - y sg)
+        float p = dsacc[r] * fmaf(alpha, fmaf(-y, sg, y), sg);
+        if constexpr (kMasked) {
           if (!((mrow[i] >> n) & 1u)) {
             y = 0.f;
             p = 0.f;
           }
-          yb[mq * 2 + (r >> 3)][r & 7] = (__bf16)y;
-          pb[mq * 2 + (r >> 3)][r & 7] = (__bf16)p;
         }
+        yb[r >> 3][r & 7] = (__bf16)y;
+        pb[r >> 3][r & 7] = (__bf16)p;
       }
     }
     // dV^T += dO^T Y and dK^T += Q^T P: A operands by transpose reads, query
-    // rows 16ss + 4g + {0..3} and 16ss + 8 + 4g + {0..3} (ss = 2mq + half)
+    // rows 16hh + 4g + {0..3} and 16hh + 8 + 4g + {0..3}
 #pragma unroll
-    for (int ss = 0; ss < 4; ++ss) {
+    for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
       for (int mb = 0; mb < kD / 32; ++mb) {
-        const int off = tr_off + 16 * ss * kQStr + mb * 32;
+        const int off = tr_off + 16 * hh * kQStr + mb * 32;
         const bf16x8 ag = concat4(lds_read_tr(&sG[off]), lds_read_tr(&sG[off + 8 * kQStr]));
-        dvacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, yb[ss], dvacc[mb], 0, 0, 0);
+        dvacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, yb[hh], dvacc[mb], 0, 0, 0);
         const bf16x8 aq = concat4(lds_read_tr(&sQ[off]), lds_read_tr(&sQ[off + 8 * kQStr]));
-        dkacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, pb[ss], dkacc[mb], 0, 0, 0);
+        dkacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, pb[hh], dkacc[mb], 0, 0, 0);
       }
     }
-    __syncthreads();
-  }
+  };
+
+  const int nrb = (L + kRB - 1) / kRB;
+  const int4* env = P.env + (int64_t)P.rb_off[b] * ni;
+  // two passes over the row blocks that reach these keys: first those some
+  // rows see only partly (per-element mask), then those every row sees whole
+  auto pass = [&](auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
+    for (int rb = 0; rb < nrb; ++rb) {
+      bool live, full;
+      block_vs_cols(env + (int64_t)rb * ni, ni, c0, c1, live, full);
+      if (!live || full == kMasked) continue;
+      for (int half = 0; half < kRB / kKvBM; ++half) {
+        const int q0 = rb * kRB + half * kKvBM;
+        if (q0 >= L) break;
+        const int rows = min(kKvBM, L - q0);
+        const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qh + (int64_t)q0 * rs, rows, rs2, kD * 2);
+        const __amdgpu_buffer_rsrc_t rg = rows_rsrc(gh + (int64_t)q0 * rs, rows, rs2, kD * 2);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint4 a = buf_load16(rq, voff + 16 * i * rs2);
+          const uint4 c = buf_load16(rg, voff + 16 * i * rs2);
+          *reinterpret_cast<uint4*>(&sQ[(lrow + 16 * i) * kQStr + lcol]) = a;
+          *reinterpret_cast<uint4*>(&sG[(lrow + 16 * i) * kQStr + lcol]) = c;
+        }
+        if constexpr (kMasked) {
+          if (lane < kKvBM) {
+            // row q0 + lane: visibility of this wave's 32 key columns
+            int lo[kMaxNI], hi[kMaxNI];
+#pragma unroll
+            for (int j = 0; j < kMaxNI; ++j) {
+              lo[j] = L;
+              hi[j] = 0;
+              if (j < ni) row_interval_rsrc(func + s, P.total, q0 + lane, j, L, lo[j], hi[j]);
+            }
+            sMask[wave][lane] = col_mask32(lo, hi, ni, c0 + wave * 32);
+          }
+        }
+        __syncthreads();
+        step(masked);
+        __syncthreads();
+      }
+    }
+  };
+  pass(std::true_type{});
+  pass(std::false_type{});
 
   // epilogue: lane holds d = mb*32 + j*8 + g*4 + 0..3 of key row `col`
   if (col_ok) {
@@ -209,26 +221,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_kv(
   }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void k_bwd_q(
+__global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
     Prep P, const int4* __restrict__ units, const int* __restrict__ unit_count, int H,
     const int32_t* __restrict__ func, int nfunc, float alpha, float out_scale) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[kQBN * kKStr];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kQBN * kKStr];
+  __shared__ int sPart[kListWin], sFull[kListWin];
+  __shared__ int sCount[2];
+  __shared__ Envelope sEnv;
 
   const int slot = xcd_slot(blockIdx.x, *unit_count);
   if (slot < 0) return;
   const int4 u = units[slot];
-  const int b = u.x, qt = u.y, h = u.z;
-  const int64_t s = P.so[b];
-  const int L = (int)(P.so[b + 1] - s);
+  const int b = uniform(u.x), qt = uniform(u.y), h = uniform(u.z);
+  const int64_t s = uniform(P.so[b]);
+  const int L = uniform((int)(P.so[b + 1] - s));
   const int r0 = qt * kQBM;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
   const int ni = (nfunc + 1) / 2;
   const int64_t rs = (int64_t)H * kD;
+  const int rs2 = H * kD * 2;
   const float c_exp = -alpha * kLog2e;
 
   const int row = r0 + wave * 32 + n;
@@ -250,33 +266,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_q(
     hi[j] = 0;
     if (j < ni && row_ok) row_interval(func, P.total, s + row, j, L, lo[j], hi[j]);
   }
-  TileRanges R;
-  tile_ranges(P, b, r0, kQBM, L, ni, kQBN, R);
+  if (tid == 0) rows_envelope(P, b, r0, kQBM, L, ni, sEnv);
+  __syncthreads();
+  int t_begin, t_end;
+  envelope_tile_span(sEnv, ni, kQBN, t_begin, t_end);
 
   f32x16 dqacc[kD / 32];
 #pragma unroll
   for (int mb = 0; mb < kD / 32; ++mb) dqacc[mb] = f32x16{};
 
+  const uint16_t* kh = k + s * rs + (int64_t)h * kD;
+  const uint16_t* vh = v + s * rs + (int64_t)h * kD;
   const int krow = tid >> 4, kcol = (tid & 15) * 8;
+  const int voff = krow * rs2 + kcol * 2;
   const int grp = lane >> 4, gl = lane & 15;
   const int tr_off = (4 * (grp >> 1) + (gl >> 2)) * kKStr + (grp & 1) * 16 + 4 * (gl & 3);
 
-  for (int t = next_live(R, ni, 0); t >= 0; t = next_live(R, ni, t + 1)) {
-    const int c0 = t * kQBN;
-    const bool full = tile_full(R, ni, c0, min(c0 + kQBN, L));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kv = krow + 16 * i;
-      uint4 a = make_uint4(0, 0, 0, 0), c = make_uint4(0, 0, 0, 0);
-      if (c0 + kv < L) {
-        a = *reinterpret_cast<const uint4*>(k + (s + c0 + kv) * rs + (int64_t)h * kD + kcol);
-        c = *reinterpret_cast<const uint4*>(v + (s + c0 + kv) * rs + (int64_t)h * kD + kcol);
-      }
-      *reinterpret_cast<uint4*>(&sK[kv * kKStr + kcol]) = a;
-      *reinterpret_cast<uint4*>(&sV[kv * kKStr + kcol]) = c;
-    }
-    __syncthreads();
-
+  auto compute = [&](int c0, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
     f32x16 sacc[2], dsacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -295,16 +302,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_q(
     bf16x8 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      uint32_t mg = 0xffffffffu;
-      if (!full) mg = col_mask32(lo, hi, ni, c0 + kb * 32) >> (g * 4);
+      uint32_t mg = 0;
+      if constexpr (kMasked) mg = col_mask32(lo, hi, ni, c0 + kb * 32) >> (g * 4);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float x = sacc[kb][r];
         const float sg = logistic_scaled(x, c_exp);
-        const float ax = alpha * x;
-        float p = dsacc[kb][r] * (sg * (1.0f + ax * (1.0f - sg)));
-        const int bit = (r >> 2) * 8 + (r & 3);
-        if (!((mg >> bit) & 1u)) p = 0.f;
+        // silu'(alpha x) = sg + alpha * x sg (1 - sg)
+        const float y = x * sg;
+        float p = dsacc[kb][r] * fmaf(alpha, fmaf(-y, sg, y), sg);
+        if constexpr (kMasked) {
+          const int bit = (r >> 2) * 8 + (r & 3);
+          if (!((mg >> bit) & 1u)) p = 0.f;
+        }
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
     }
@@ -317,7 +327,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_q(
         dqacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ss], dqacc[mb], 0, 0, 0);
       }
     }
+  };
+
+  auto walk = [&](const int* list, int cnt, auto masked) {
+    for (int i = 0; i < cnt; ++i) {
+      const int c0 = list[i] * kQBN;
+      const int rows = min(kQBN, L - c0);
+      const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kh + (int64_t)c0 * rs, rows, rs2, kD * 2);
+      const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vh + (int64_t)c0 * rs, rows, rs2, kD * 2);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const uint4 a = buf_load16(rk, voff + 16 * ii * rs2);
+        const uint4 c = buf_load16(rv, voff + 16 * ii * rs2);
+        *reinterpret_cast<uint4*>(&sK[(krow + 16 * ii) * kKStr + kcol]) = a;
+        *reinterpret_cast<uint4*>(&sV[(krow + 16 * ii) * kKStr + kcol]) = c;
+      }
+      __syncthreads();
+      compute(c0, masked);
+      __syncthreads();
+    }
+  };
+
+  for (int w0 = t_begin; w0 < t_end; w0 += kListWin) {
+    if (wave == 0) {
+      int np, nf;
+      tile_window(sEnv, ni, kQBN, L, w0, t_end, sPart, sFull, np, nf);
+      if (lane == 0) {
+        sCount[0] = np;
+        sCount[1] = nf;
+      }
+    }
     __syncthreads();
+    walk(sPart, sCount[0], std::true_type{});
+    walk(sFull, sCount[1], std::false_type{});
   }
 
   if (row_ok) {

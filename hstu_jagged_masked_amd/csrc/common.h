@@ -156,6 +156,15 @@ __device__ __forceinline__ int xcd_slot(int bid, int n) {
   return (k < per && slot < n) ? slot : -1;
 }
 
+// Values every lane of the wave holds in common, moved to scalar registers.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Largest index i in [0, n] with a[i] <= x (a nondecreasing, a[0] <= x).
 template <typename T>
 __device__ __forceinline__ int upper_index(const T* a, int n, T x) {

@@ -4,11 +4,12 @@
 //   x_ij = <q_i, k_j>   (so that alpha * y_ij = silu(alpha x_ij)).
 //
 // One workgroup (4 waves) owns 128 query rows of one (sequence, head); wave w
-// owns rows [32w, 32w+32) of the tile.  The workgroup walks the key tiles of
-// 64 columns that its row blocks' interval envelopes reach (the rest are never
-// loaded), in increasing order:
-//   1. K and V tiles -> LDS, both row-major, staged through registers so the
-//      next tile's global loads overlap this tile's math;
+// owns rows [32w, 32w+32) of the tile.  Wave 0 lists, 64 tiles at a time, the
+// key tiles of 64 columns that the rows' interval envelopes reach (the rest are
+// never loaded) and flags the tiles every row sees whole.  For each listed tile:
+//   1. K and V tiles -> LDS, both row-major, through registers so the next
+//      tile's global loads overlap this tile's math; buffer loads whose range
+//      check zero-fills rows past the sequence end;
 //   2. S^T = K Q^T on MFMA: A = K from LDS, B = Q^T from registers (each lane
 //      keeps its query row's 128 dims), so the accumulator holds one query row
 //      per lane and 16 key columns;
@@ -20,6 +21,8 @@
 // The key index order inside each 16-wide MFMA step is permuted identically
 // in both operands (it is a sum), which is what lets step 3 feed step 4
 // without any data movement.
+#include <type_traits>
+
 #include "common.h"
 #include "tiles.h"
 
@@ -30,8 +33,8 @@ namespace {
 constexpr int kD = 128;
 constexpr int kBM = 128;             // query rows per workgroup
 constexpr int kBN = 64;              // key columns per tile
-constexpr int kKStr = kD + 8;        // LDS row stride of K (bf16): 272 B, spreads banks
-constexpr int kVStr = kD + 16;       // LDS row stride of V (bf16): 288 B, for transpose reads
+constexpr int kKStr = kD + 8;        // LDS row stride of K (bf16): 272 B, b128 reads conflict-free
+constexpr int kVStr = kD + 32;       // LDS row stride of V (bf16): 320 B, transpose reads conflict-free
 constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
@@ -41,19 +44,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
     float alpha, float out_scale) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[kBN * kKStr];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kBN * kVStr];
+  __shared__ int sPart[kListWin], sFull[kListWin];
+  __shared__ int sCount[2];
+  __shared__ Envelope sEnv;
 
   const int slot = xcd_slot(blockIdx.x, *unit_count);
   if (slot < 0) return;
   const int4 u = units[slot];
-  const int b = u.x, qt = u.y, h = u.z;
-  const int64_t s = P.so[b];
-  const int L = (int)(P.so[b + 1] - s);
+  const int b = uniform(u.x), qt = uniform(u.y), h = uniform(u.z);
+  const int64_t s = uniform(P.so[b]);
+  const int L = uniform((int)(P.so[b + 1] - s));
   const int r0 = qt * kBM;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
   const int ni = (nfunc + 1) / 2;
   const int64_t rs = (int64_t)H * kD;  // row stride (elements)
+  const int rs2 = H * kD * 2;          // row stride (bytes)
 
   // this lane's query row (B-operand column n of wave `wave`)
   const int row = r0 + wave * 32 + n;
@@ -62,13 +69,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
   {
     const uint16_t* qp = q + (s + row) * rs + (int64_t)h * kD + g * 8;
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      if (row_ok) {
-        qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
-      } else {
-        qf[ks] = bf16x8{};
-      }
-    }
+    for (int ks = 0; ks < kD / 16; ++ks)
+      qf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + ks * 16) : bf16x8{};
   }
   int lo[kMaxNI], hi[kMaxNI];
 #pragma unroll
@@ -78,29 +80,32 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
     if (j < ni && row_ok) row_interval(func, P.total, s + row, j, L, lo[j], hi[j]);
   }
 
-  TileRanges R;
-  tile_ranges(P, b, r0, kBM, L, ni, kBN, R);
+  if (tid == 0) rows_envelope(P, b, r0, kBM, L, ni, sEnv);
+  __syncthreads();
+  int t_begin, t_end;
+  envelope_tile_span(sEnv, ni, kBN, t_begin, t_end);
 
   f32x16 oacc[kD / 32];
 #pragma unroll
   for (int mb = 0; mb < kD / 32; ++mb) oacc[mb] = f32x16{};
 
   const float c_exp = -alpha * kLog2e;
+  const uint16_t* kh = k + s * rs + (int64_t)h * kD;
+  const uint16_t* vh = v + s * rs + (int64_t)h * kD;
 
-  // staging registers for one K/V tile: rows krow + 16i, dims kcol..kcol+7
+  // staging: thread loads rows krow + 16i, dims kcol..kcol+7, of K and V
   const int krow = tid >> 4, kcol = (tid & 15) * 8;
+  const int voff = krow * rs2 + kcol * 2;
   uint4 kreg[4], vreg[4];
   auto load_tile = [&](int t) {
     const int c0 = t * kBN;
+    const int rows = min(kBN, L - c0);
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kh + (int64_t)c0 * rs, rows, rs2, kD * 2);
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vh + (int64_t)c0 * rs, rows, rs2, kD * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kv = krow + 16 * i;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      if (c0 + kv < L)
-        kreg[i] = *reinterpret_cast<const uint4*>(k + (s + c0 + kv) * rs + (int64_t)h * kD + kcol);
-      vreg[i] = make_uint4(0, 0, 0, 0);
-      if (c0 + kv < L)
-        vreg[i] = *reinterpret_cast<const uint4*>(v + (s + c0 + kv) * rs + (int64_t)h * kD + kcol);
+      kreg[i] = buf_load16(rk, voff + 16 * i * rs2);
+      vreg[i] = buf_load16(rv, voff + 16 * i * rs2);
     }
   };
   auto store_tile = [&]() {
@@ -114,47 +119,37 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
   // group points at row j/4 of a 4-row block, columns 4*(j%4)..+3
   const int grp = lane >> 4, gl = lane & 15;
   const uint16_t* vbase = &sV[(4 * (grp >> 1) + (gl >> 2)) * kVStr + (grp & 1) * 16 + 4 * (gl & 3)];
+  const uint16_t* kbase = &sK[n * kKStr + g * 8];
 
-  int t = next_live(R, ni, 0);
-  if (t >= 0) {
-    load_tile(t);
-    store_tile();
-  }
-  __syncthreads();
-  while (t >= 0) {
-    const int tn = next_live(R, ni, t + 1);
-    if (tn >= 0) load_tile(tn);
-    const int c0 = t * kBN;
-    const bool full = tile_full(R, ni, c0, min(c0 + kBN, L));
-
-    // S^T = K Q^T for the 64 columns (two 32-column halves)
+  // one tile: S^T, SiLU (+ mask), O^T += V^T Y^T
+  auto compute = [&](int c0, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x16{};
-      const uint16_t* kp = &sK[(kb * 32 + n) * kKStr + g * 8];
 #pragma unroll
       for (int ks = 0; ks < kD / 16; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + ks * 16);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kbase + kb * 32 * kKStr + ks * 16);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
-    // y = x * logistic(alpha x), masked, -> bf16 B operands
     bf16x8 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      uint32_t mg = 0xffffffffu;
-      if (!full) mg = col_mask32(lo, hi, ni, c0 + kb * 32) >> (g * 4);
+      uint32_t mg = 0;
+      if constexpr (kMasked) mg = col_mask32(lo, hi, ni, c0 + kb * 32) >> (g * 4);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float x = sacc[kb][r];
         float y = x * logistic_scaled(x, c_exp);
-        const int bit = (r >> 2) * 8 + (r & 3);
-        if (!((mg >> bit) & 1u)) y = 0.f;
+        if constexpr (kMasked) {
+          const int bit = (r >> 2) * 8 + (r & 3);
+          if (!((mg >> bit) & 1u)) y = 0.f;
+        }
         pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)y;
       }
     }
-    // O^T += V^T Y^T
     // A = V^T: lane (d = mb*32 + n, half g) takes key rows 16ss + 4g + {0..3}
     // and 16ss + 8 + 4g + {0..3}, the same order the Y^T operand uses.
 #pragma unroll
@@ -168,10 +163,36 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
         oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[ss], oacc[mb], 0, 0, 0);
       }
     }
+  };
+
+  // walk a list of tiles: the next tile's loads are in flight while this one
+  // is computed
+  auto walk = [&](const int* list, int cnt, auto masked) {
+    if (cnt == 0) return;
+    load_tile(list[0]);
+    store_tile();
     __syncthreads();
-    if (tn >= 0) store_tile();
+    for (int i = 0; i < cnt; ++i) {
+      if (i + 1 < cnt) load_tile(list[i + 1]);
+      compute(list[i] * kBN, masked);
+      __syncthreads();
+      if (i + 1 < cnt) store_tile();
+      __syncthreads();
+    }
+  };
+
+  for (int w0 = t_begin; w0 < t_end; w0 += kListWin) {
+    if (wave == 0) {
+      int np, nf;
+      tile_window(sEnv, ni, kBN, L, w0, t_end, sPart, sFull, np, nf);
+      if (lane == 0) {
+        sCount[0] = np;
+        sCount[1] = nf;
+      }
+    }
     __syncthreads();
-    t = tn;
+    walk(sPart, sCount[0], std::true_type{});
+    walk(sFull, sCount[1], std::false_type{});
   }
 
   // epilogue: lane holds O[row][mb*32 + j*8 + g*4 + 0..3]
@@ -200,7 +221,7 @@ hipError_t launch_mfma_fwd(const void* q, const void* k, const void* v, void* o,
   hipLaunchKernelGGL(k_fwd_bf16, dim3(U.cap), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), P, U.list,
-                     P.flags + 4, H, func, nfunc, alpha, alpha * inv_max_len);
+                     P.flags + kSlotFwdUnits, H, func, nfunc, alpha, alpha * inv_max_len);
   return hipGetLastError();
 }
 

@@ -1,6 +1,12 @@
-// Tile-level helpers shared by the MFMA kernels: key-tile ranges from the
-// row-block interval envelopes, whole-tile visibility tests and per-row
-// column bitmasks for tiles some rows see only partly.
+// Tile-level helpers shared by the MFMA kernels:
+//   * the interval envelope of a block of query rows (from the per-row-block
+//     envelopes the decoder wrote), and the key tiles it reaches;
+//   * a per-workgroup list of those key tiles in LDS, built 64 tiles at a time
+//     by one wave with a ballot, each entry flagged "full" when every valid
+//     row of the block sees the whole tile (no per-element mask needed);
+//   * per-row column bitmasks for tiles some rows see only partly;
+//   * buffer resources whose hardware range check returns zeros for rows past
+//     the end of a sequence (no predication on the loads).
 #pragma once
 
 #include "common.h"
@@ -8,6 +14,7 @@
 namespace hstu {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kListWin = 64;        // key tiles per list window
 
 __device__ __forceinline__ uint32_t low_bits(int n) {  // n in [0, 32]
   return n >= 32 ? 0xffffffffu : ((1u << n) - 1u);
@@ -27,68 +34,81 @@ __device__ __forceinline__ uint32_t col_mask32(const int* lo, const int* hi, int
   return m;
 }
 
-struct TileRanges {
-  int a[kMaxNI], e[kMaxNI];      // live key tiles per interval, inclusive (empty: a > e)
-  int ilo[kMaxNI], ihi[kMaxNI];  // intersection envelope (columns)
-  int tmax;
+// Union [ulo, uhi) and intersection [ilo, ihi) envelopes of every interval
+// over the query rows [r0, r0 + rows) (a whole number of row blocks).
+struct Envelope {
+  int ulo[kMaxNI], uhi[kMaxNI], ilo[kMaxNI], ihi[kMaxNI];
 };
 
-__device__ __forceinline__ bool tile_live(const TileRanges& R, int ni, int t) {
-  bool r = false;
-#pragma unroll
-  for (int j = 0; j < kMaxNI; ++j)
-    if (j < ni) r = r || (t >= R.a[j] && t <= R.e[j]);
-  return r;
-}
-
-__device__ __forceinline__ bool tile_full(const TileRanges& R, int ni, int c0, int c1) {
-  bool r = false;
-#pragma unroll
-  for (int j = 0; j < kMaxNI; ++j)
-    if (j < ni) r = r || (R.ilo[j] <= c0 && c1 <= R.ihi[j]);
-  return r;
-}
-
-__device__ __forceinline__ int next_live(const TileRanges& R, int ni, int t) {
-  for (; t <= R.tmax; ++t)
-    if (tile_live(R, ni, t)) return t;
-  return -1;
-}
-
-// Envelope of the query rows [r0, r0 + rows) (whole row blocks) -> key tiles.
-__device__ __forceinline__ void tile_ranges(const Prep& P, int b, int r0, int rows, int L, int ni,
-                                            int bn, TileRanges& R) {
+__device__ __forceinline__ void rows_envelope(const Prep& P, int b, int r0, int rows, int L,
+                                              int ni, Envelope& E) {
   const int rb0 = r0 / kRB;
   const int nrb = min((rows + kRB - 1) / kRB, (L - r0 + kRB - 1) / kRB);
   const int4* env = P.env + (int64_t)(P.rb_off[b] + rb0) * ni;
-  R.tmax = -1;
 #pragma unroll
   for (int j = 0; j < kMaxNI; ++j) {
-    int ulo = L, uhi = 0, ilo = INT32_MIN, ihi = INT32_MAX;
+    E.ulo[j] = L;
+    E.uhi[j] = 0;
+    E.ilo[j] = INT32_MIN;
+    E.ihi[j] = INT32_MAX;
     if (j < ni) {
       for (int r = 0; r < nrb; ++r) {
         const int4 v = env[r * ni + j];
-        ulo = min(ulo, v.x);
-        uhi = max(uhi, v.y);
-        ilo = max(ilo, v.z);
-        ihi = min(ihi, v.w);
+        E.ulo[j] = min(E.ulo[j], v.x);
+        E.uhi[j] = max(E.uhi[j], v.y);
+        E.ilo[j] = max(E.ilo[j], v.z);
+        E.ihi[j] = min(E.ihi[j], v.w);
       }
     }
-    if (ulo < uhi) {
-      R.a[j] = ulo / bn;
-      R.e[j] = (uhi - 1) / bn;
-      R.tmax = max(R.tmax, R.e[j]);
-    } else {
-      R.a[j] = 1;
-      R.e[j] = 0;
-    }
-    R.ilo[j] = ilo;
-    R.ihi[j] = ihi;
   }
 }
 
+// Key tiles [t_begin, t_end) that may hold visible columns.
+__device__ __forceinline__ void envelope_tile_span(const Envelope& E, int ni, int bn, int& t_begin,
+                                                   int& t_end) {
+  t_begin = INT32_MAX;
+  t_end = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxNI; ++j) {
+    if (j < ni && E.ulo[j] < E.uhi[j]) {
+      t_begin = min(t_begin, E.ulo[j] / bn);
+      t_end = max(t_end, (E.uhi[j] - 1) / bn + 1);
+    }
+  }
+  if (t_end <= t_begin) t_begin = t_end = 0;
+}
 
-// Whether row block `rb` (envelope row `env`) reaches key columns [c0, c1),
+// Wave-level: lists the live tiles of [w0, min(w0 + 64, w1)) in two arrays,
+// those some valid row sees only partly (part[0..*n_part)) and those every
+// valid row sees whole (full[0..*n_full)), in increasing order.  Must be
+// called by a whole wave; the counts are returned in every lane.
+__device__ __forceinline__ void tile_window(const Envelope& E, int ni, int bn, int L, int w0,
+                                            int w1, int* part, int* full_list, int& n_part,
+                                            int& n_full) {
+  const int lane = threadIdx.x & 63;
+  const int t = w0 + lane;
+  const int c0 = t * bn, c1 = min(c0 + bn, L);
+  bool live = false, full = false;
+  if (t < w1) {
+#pragma unroll
+    for (int j = 0; j < kMaxNI; ++j) {
+      if (j < ni) {
+        live = live || (E.ulo[j] < E.uhi[j] && E.ulo[j] < c1 && E.uhi[j] > c0);
+        full = full || (E.ilo[j] <= c0 && c1 <= E.ihi[j]);
+      }
+    }
+  }
+  full = full && live;
+  const bool partial = live && !full;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint64_t mp = __ballot(partial), mf = __ballot(full);
+  if (partial) part[__popcll(mp & below)] = t;
+  if (full) full_list[__popcll(mf & below)] = t;
+  n_part = __popcll(mp);
+  n_full = __popcll(mf);
+}
+
+// Whether row block `rb` (its envelope row `env`) reaches key columns [c0, c1),
 // and whether every valid row of it sees all of them.
 __device__ __forceinline__ void block_vs_cols(const int4* env, int ni, int c0, int c1, bool& live,
                                               bool& full) {
@@ -102,6 +122,46 @@ __device__ __forceinline__ void block_vs_cols(const int4* env, int ni, int c0, i
       full = full || (e.z <= c0 && c1 <= e.w);
     }
   }
+}
+
+// Buffer resource over `rows` rows of `row_bytes` bytes starting at `base`,
+// exposing only the first `width_bytes` of the last row: reads at
+// row*row_bytes + col (col < width_bytes) return data for row < rows and zeros
+// past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int rows,
+                                                             int row_bytes, int width_bytes) {
+  const int n = rows > 0 ? (rows - 1) * row_bytes + width_bytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// Clipped interval j of local row r of a sequence of length L whose func
+// columns start at fseq (= func + first row of the sequence); empty intervals
+// (and rows r >= L) come back as lo = L, hi = 0.  Reads func through buffer
+// resources so the only per-lane state is the 32-bit offset r*4.
+__device__ __forceinline__ void row_interval_rsrc(const int32_t* fseq, int64_t total, int r, int j,
+                                                  int L, int& lo, int& hi) {
+  int a = 0, b;
+  const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(fseq + (int64_t)(2 * j) * total), (short)0, L * 4, 0x00020000);
+  b = __builtin_amdgcn_raw_buffer_load_b32(re, r * 4, 0, 0);
+  if (j > 0) {
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(fseq + (int64_t)(2 * j - 1) * total), (short)0, L * 4, 0x00020000);
+    a = __builtin_amdgcn_raw_buffer_load_b32(rl, r * 4, 0, 0);
+  }
+  a = max(a, 0);
+  b = min(b, L);
+  if (b <= a || r >= L) {
+    a = L;
+    b = 0;
+  }
+  lo = a;
+  hi = b;
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voffset) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voffset, 0, 0);
+  return __builtin_bit_cast(uint4, v);
 }
 
 }  // namespace hstu
