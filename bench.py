@@ -20,7 +20,6 @@ Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -39,27 +38,18 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # algorithmic flops per visible pair and head, as multiples of D
 KERNEL_FLOPS_PER_PAIR = {"k_fwd_bf16": 4, "k_bwd_kv": 8, "k_bwd_q": 2}
-KERNEL_SOURCES = {"k_fwd_bf16": ["fwd.hip"], "k_bwd_kv": ["bwd.hip"], "k_bwd_q": ["bwd.hip"],
-                  "k_targets_fwd": ["targets.hip"], "k_targets_bwd": ["targets.hip"]}
-COMMON_SOURCES = ["common.h", "tiles.h"]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_digest(kernel: str) -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "hstu_jagged_masked_amd", "csrc")
-    for name in KERNEL_SOURCES.get(kernel, []) + COMMON_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
-
-
 def measured_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current source of that kernel; else None."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE / WRITE_SIZE scaled by a copy-kernel calibration), if it was
+    taken on the current source of that kernel; else None."""
+    from hstu_jagged_masked_amd import profiling
+
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as f:
@@ -67,9 +57,9 @@ def measured_traffic(kernel: str):
     except (OSError, ValueError):
         return None
     rec = data.get(kernel)
-    if not rec or rec.get("source_sha256") != source_digest(kernel):
+    if not rec or rec.get("source_sha256") != profiling.source_digest(kernel):
         return None
-    return rec.get("bytes_per_launch")
+    return round(rec["bytes_per_launch"])
 
 
 def make_inputs(cfg, device, targets=False):
@@ -153,6 +143,9 @@ def main():
     ap.add_argument("--targets-steps", type=int, default=20)
     ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences in the CPU oracle sample (0 disables it)")
+    ap.add_argument("--calib-copy-mib", type=int, default=1024,
+                    help="size of a plain device-to-device copy run once before timing; "
+                         "counter runs scale HBM byte counters by it (0 disables it)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -177,6 +170,13 @@ def main():
     pairs = int(pairs_t.item())
     log(f"[bench] visible pairs per head: {pairs}")
 
+    if args.calib_copy_mib > 0:
+        nbytes = args.calib_copy_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=device).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     run_steps(hj, t, cfg, args.warmup)
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
@@ -211,6 +211,8 @@ def main():
     # fwd streams K, V; bwd streams K, V in and dK, dV out (bf16)
     t_bytes = 6.0 * T * H * D * 2
     targets = {"ms_per_step": round(t_ms, 4), "speedup_vs_full": round(ms / t_ms, 2),
+               "traffic_bytes_per_launch": {k: measured_traffic(k)
+                                            for k in ("k_targets_fwd", "k_targets_bwd")},
                "algorithmic_gb": round(t_bytes / 1e9, 3),
                "gbs": round(t_bytes / (t_ms * 1e-3) / 1e9, 1),
                "frac_hbm_peak": round(t_bytes / (t_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

@@ -1,0 +1,143 @@
+"""Summaries of rocprofv3 output for the HSTU attention kernels.
+
+    python -m hstu_jagged_masked_amd.profiling stats DIR          # --kernel-trace --stats CSVs
+    python -m hstu_jagged_masked_amd.profiling pmc DIR [DIR ...]  # --pmc counter CSVs
+    python -m hstu_jagged_masked_amd.profiling traffic FETCH_DIR WRITE_DIR OUT.json
+
+``stats`` prints per-kernel launch count and average / total duration.
+``pmc`` prints the average of each counter per dispatch, per kernel.
+``traffic`` turns FETCH_SIZE and WRITE_SIZE (KiB per dispatch) into HBM bytes per
+launch of each MFMA/streaming kernel.  The raw counters are scaled by the
+factor that maps the same counter of a plain device-to-device copy of known
+size (the ``bench.py`` calibration copy, a device-to-device hipMemcpy that the
+runtime performs with its copy kernel; the largest such dispatch in the run)
+onto its true byte count, read and write separately.  The JSON records the
+sha256 of each kernel's source so a reader can tell whether it is still current.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNELS = ("k_fwd_bf16", "k_bwd_kv", "k_bwd_q", "k_targets_fwd", "k_targets_bwd")
+KERNEL_SOURCES = {"k_fwd_bf16": ["fwd.hip"], "k_bwd_kv": ["bwd.hip"], "k_bwd_q": ["bwd.hip"],
+                  "k_targets_fwd": ["targets.hip"], "k_targets_bwd": ["targets.hip"]}
+COMMON_SOURCES = ["common.h", "tiles.h"]
+COPY_KERNEL = "__amd_rocclr_copybuffer"  # the HIP runtime's device-to-device copy kernel
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES.get(kernel, []) + COMMON_SOURCES:
+        with open(os.path.join(PKG, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def short_name(name: str) -> str:
+    m = re.search(r"(k_\w+)", name)
+    if m and "hstu" in name:
+        return m.group(1)
+    return name.split("(")[0][-60:]
+
+
+def read_rows(path_glob):
+    rows = []
+    for f in sorted(glob.glob(path_glob, recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def stats(directory: str) -> str:
+    rows = read_rows(os.path.join(directory, "**", "*kernel_stats.csv"))
+    out = ["kernel                     calls   avg_ms      total_ms   pct"]
+    for r in rows:
+        name = short_name(r["Name"])
+        out.append(f"{name:26s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e6:9.4f} "
+                   f"{float(r['TotalDurationNs']) / 1e6:11.3f} {float(r['Percentage']):6.2f}")
+    return "\n".join(out)
+
+
+def pmc_table(directories):
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in directories:
+        for r in read_rows(os.path.join(d, "**", "*counter_collection.csv")):
+            agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return agg
+
+
+def pmc(directories) -> str:
+    agg = pmc_table(directories)
+    out = []
+    for name, counters in sorted(agg.items(), key=lambda kv: short_name(kv[0])):
+        short = short_name(name)
+        if short not in KERNELS:
+            continue
+        out.append(f"== {short}")
+        for c, vals in sorted(counters.items()):
+            out.append(f"   {c:32s} {sum(vals) / len(vals):.6g}")
+    return "\n".join(out)
+
+
+def _calibration(agg, counter):
+    """(counter value, true bytes) of the largest copy kernel dispatch."""
+    best = None
+    for name, counters in agg.items():
+        if COPY_KERNEL not in name.lower() or counter not in counters:
+            continue
+        v = max(counters[counter])
+        if best is None or v > best:
+            best = v
+    return best
+
+
+def traffic(fetch_dir: str, write_dir: str, out_path: str, copy_bytes: int) -> dict:
+    fa, wa = pmc_table([fetch_dir]), pmc_table([write_dir])
+    f_cal, w_cal = _calibration(fa, "FETCH_SIZE"), _calibration(wa, "WRITE_SIZE")
+    if not f_cal or not w_cal:
+        raise SystemExit("no calibration copy kernel found in the counter runs")
+    f_scale = copy_bytes / (f_cal * 1024.0)
+    w_scale = copy_bytes / (w_cal * 1024.0)
+    result = {"_calibration": {"copy_bytes": copy_bytes, "fetch_kib": f_cal, "write_kib": w_cal,
+                               "fetch_scale": f_scale, "write_scale": w_scale}}
+    for name in set(fa) | set(wa):
+        short = short_name(name)
+        if short not in KERNELS:
+            continue
+        fk = fa.get(name, {}).get("FETCH_SIZE")
+        wk = wa.get(name, {}).get("WRITE_SIZE")
+        if not fk or not wk:
+            continue
+        fb = sum(fk) / len(fk) * 1024.0 * f_scale
+        wb = sum(wk) / len(wk) * 1024.0 * w_scale
+        result[short] = {"fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                         "bytes_per_launch": fb + wb, "source_sha256": source_digest(short)}
+    with open(out_path, "w") as f:
+        json.dump(result, f, indent=1, sort_keys=True)
+    return result
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[0] == "stats":
+        print(stats(argv[1]))
+    elif len(argv) >= 2 and argv[0] == "pmc":
+        print(pmc(argv[1:]))
+    elif len(argv) >= 4 and argv[0] == "traffic":
+        copy_bytes = int(argv[4]) if len(argv) > 4 else 1 << 30
+        print(json.dumps(traffic(argv[1], argv[2], argv[3], copy_bytes), indent=1))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
