@@ -1,0 +1,178 @@
+"""GPU parity at the full workload sizes, through the same entry points and
+launch configuration bench.py times.
+
+Every output of a sequence (O, dQ, dK, dV of its rows) depends only on that
+sequence's rows, so the oracle run on a few whole sequences gives exact
+expected values for them; the small SLA workloads are checked in full.
+Visible counts are checked for every row against closed forms where the
+mask has one, else against the oracle on the sampled sequences.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def hj():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import hstu_jagged_masked_amd as hj
+
+    hj.library()
+    return hj
+
+
+def device_inputs(cfg, targets=False):
+    lengths = cfg["lengths"]
+    off = wl.offsets_from_lengths(lengths)
+    T = int(off[-1])
+    B, H, D = len(lengths), cfg["H"], cfg["D"]
+    seed = cfg["seed"]
+    rq = B if targets else T
+    dt = torch.bfloat16
+    t = {
+        "off": torch.from_numpy(off).to(DEV),
+        "k": wl.normal_device((T, H, D), seed * 10 + 1, dt, DEV),
+        "v": wl.normal_device((T, H, D), seed * 10 + 2, dt, DEV),
+        "q": wl.normal_device((rq, H, D), seed * 10 + (5 if targets else 0), dt, DEV),
+        "do": wl.normal_device((rq, H, D), seed * 10 + (6 if targets else 3), dt, DEV),
+    }
+    return t, off
+
+
+def check(name, got, want):
+    got = got.float().cpu().numpy().astype(np.float64)
+    assert got.shape == want.shape, name
+    assert np.all(np.isfinite(got)), f"{name}: non-finite"
+    err = float(np.max(np.abs(got - want))) if want.size else 0.0
+    scale = float(np.max(np.abs(want))) if want.size else 0.0
+    assert err <= 2e-2 * max(1.0, scale), f"{name}: max abs err {err:.3e}"
+    assert err <= 2e-2 * scale, f"{name}: rel err {err / scale:.3e}"
+    print(f"  {name}: max abs err {err:.3e}, rel {err / max(scale, 1e-30):.3e}", flush=True)
+
+
+def to64(x):
+    return x.float().cpu().numpy().astype(np.float64)
+
+
+def run_full(hj, cfg, func_np, seqs, nfunc_label=""):
+    """fwd+bwd on the whole workload; oracle on the sequences `seqs`."""
+    t, off = device_inputs(cfg)
+    func = torch.from_numpy(func_np).to(DEV)
+    o = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], func, cfg["alpha"], cfg["max_len"])
+    dq, dk, dv = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
+                             cfg["max_len"])
+    torch.cuda.synchronize()
+    rows, sub_off = oracle.subset(off, seqs)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    pick = lambda x: to64(x.index_select(0, rows_t))  # noqa: E731
+    q, k, v, do = (pick(t[n]) for n in ("q", "k", "v", "do"))
+    f_sub = np.ascontiguousarray(func_np[:, rows])
+    want_o = oracle.fwd(q, k, v, sub_off, f_sub, cfg["alpha"], cfg["max_len"])
+    want = oracle.bwd(q, k, v, do, sub_off, f_sub, cfg["alpha"], cfg["max_len"])
+    for nm, got, w in zip(("o", "dq", "dk", "dv"), (o, dq, dk, dv), (want_o,) + want):
+        check(f"{cfg['name']}{nfunc_label}.{nm}", got.index_select(0, rows_t), w)
+    return (o, dq, dk, dv), t, off
+
+
+def sample_seqs(lengths, n_extra=1):
+    order = np.argsort(lengths, kind="stable")
+    picks = [int(order[-1]), int(order[0]), int(order[len(order) // 2])]
+    picks += [int(i) for i in np.linspace(0, len(lengths) - 1, n_extra + 2)[1:-1]]
+    return sorted(set(picks))
+
+
+def test_sla_1k_full(hj):
+    cfg = wl.workload("sla_1k")
+    ls = cfg["lengths"]
+    f = cfg["func"](ls, 5)
+    run_full(hj, cfg, f, list(range(len(ls))))
+    off_t = torch.from_numpy(wl.offsets_from_lengths(ls)).to(DEV)
+    counts, tot = hj.visible_counts(off_t, torch.from_numpy(f).to(DEV), int(ls.sum()))
+    i = wl.local_rows(ls)
+    want = np.minimum(32, i + 1) + np.maximum(0, i + 1 - np.maximum(32, i - 255))
+    assert np.array_equal(counts.cpu().numpy(), want)
+    assert int(tot.item()) == 32 * 253584
+
+
+def test_sla_2k_full_and_nfunc3_bitwise(hj):
+    cfg = wl.workload("sla_2k")
+    ls = cfg["lengths"]
+    out5, t, off = run_full(hj, cfg, cfg["func"](ls, 5), list(range(len(ls))))
+    f3 = torch.from_numpy(cfg["func"](ls, 3)).to(DEV)
+    o3 = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], f3, cfg["alpha"], cfg["max_len"])
+    g3 = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], f3, cfg["alpha"], cfg["max_len"])
+    for a, b in zip(out5, (o3,) + tuple(g3)):
+        assert torch.equal(a, b), "nfunc=5 padded differs from nfunc=3"
+    _, tot = hj.visible_counts(t["off"], f3, int(off[-1]))
+    assert int(tot.item()) == 16 * 548496
+
+
+@pytest.mark.parametrize("name", ["hstu_2663", "hstu_ragged", "hstu_4086"])
+def test_hstu_layer_shapes_sampled(hj, name):
+    cfg = wl.workload(name)
+    ls = cfg["lengths"]
+    f = cfg["func"](ls, 5)
+    run_full(hj, cfg, f, sample_seqs(ls))
+    off_t = torch.from_numpy(wl.offsets_from_lengths(ls)).to(DEV)
+    counts, tot = hj.visible_counts(off_t, torch.from_numpy(f).to(DEV), int(ls.sum()))
+    assert np.array_equal(counts.cpu().numpy(), wl.local_rows(ls) + 1), "causal counts"
+    assert int(tot.item()) == int(np.sum(ls * (ls + 1) // 2))
+
+
+def test_three_interval_sampled(hj):
+    cfg = wl.workload("three_interval")
+    ls = cfg["lengths"]
+    f = cfg["func"](ls, 5)
+    seqs = sample_seqs(ls)
+    run_full(hj, cfg, f, seqs)
+    off = wl.offsets_from_lengths(ls)
+    off_t = torch.from_numpy(off).to(DEV)
+    counts, _ = hj.visible_counts(off_t, torch.from_numpy(f).to(DEV), int(off[-1]))
+    counts = counts.cpu().numpy()
+    rows, sub_off = oracle.subset(off, seqs)
+    want, _ = oracle.visible_counts(sub_off, np.ascontiguousarray(f[:, rows]))
+    assert np.array_equal(counts[rows], want)
+
+
+def test_hstu_2663_targets_only_sampled(hj):
+    """Targets-only at the production shape: candidates of 64 sampled
+    sequences checked (o, dq for the candidates; dk, dv for all their rows)."""
+    cfg = wl.workload("hstu_2663")
+    ls = cfg["lengths"]
+    f_np = cfg["func"](ls, 5)
+    t, off = device_inputs(cfg, targets=True)
+    func = torch.from_numpy(f_np).to(DEV)
+    tr_np = wl.targets_last(ls)
+    tr = torch.from_numpy(tr_np).to(DEV)
+    o = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], func, cfg["alpha"], cfg["max_len"], tr)
+    dq, dk, dv = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
+                             cfg["max_len"], tr)
+    torch.cuda.synchronize()
+    seqs = list(range(0, len(ls), 16))
+    rows, sub_off = oracle.subset(off, seqs)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    seq_t = torch.tensor(seqs, device=DEV)
+    k = to64(t["k"].index_select(0, rows_t))
+    v = to64(t["v"].index_select(0, rows_t))
+    q = to64(t["q"].index_select(0, seq_t))
+    do = to64(t["do"].index_select(0, seq_t))
+    f_sub = np.ascontiguousarray(f_np[:, rows])
+    tr_sub = tr_np[seqs]
+    want_o = oracle.fwd(q, k, v, sub_off, f_sub, cfg["alpha"], cfg["max_len"], tr_sub)
+    wq, wk, wv = oracle.bwd(q, k, v, do, sub_off, f_sub, cfg["alpha"], cfg["max_len"], tr_sub)
+    check("targets.o", o.index_select(0, seq_t), want_o)
+    check("targets.dq", dq.index_select(0, seq_t), wq)
+    check("targets.dk", dk.index_select(0, rows_t), wk)
+    check("targets.dv", dv.index_select(0, rows_t), wv)
+    counts, tot = hj.visible_counts(t["off"], func, int(off[-1]), tr)
+    assert np.array_equal(counts.cpu().numpy(), ls.astype(np.int32))
+    assert int(tot.item()) == int(ls.sum())
