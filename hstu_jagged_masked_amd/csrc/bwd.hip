@@ -12,8 +12,10 @@
 // Two kernels, each output written by exactly one workgroup (no atomics), so
 // every gradient is bitwise repeatable:
 //   k_bwd_kv  one workgroup per (sequence, head, 128 key rows); wave w owns keys
-//             [32w, 32w+32) and keeps their K and V rows in registers; it walks
-//             the 64-row query blocks whose envelopes reach its keys:
+//             [32w, 32w+32) and keeps their K and V rows in registers; wave 0
+//             lists, with a ballot, the 32-row query steps whose row blocks'
+//             envelopes reach these keys (partly seen blocks and wholly seen
+//             blocks in separate lists); for each step:
 //               S = Q K^T, dS = dO V^T          (A from LDS, B = K, V registers)
 //               y, p in registers (mask via per-row bitmasks in LDS)
 //               dV^T += dO^T Y,  dK^T += Q^T P  (A = transpose reads of the
@@ -23,6 +25,9 @@
 //               S^T = K Q^T, dS^T = V dO^T      (B = Q, dO registers)
 //               p in registers
 //               dQ^T += K^T P^T                 (A = transpose reads of K)
+// Both stage their tiles in LDS with asynchronous buffer-to-LDS DMA into two
+// stages: the next step's copy runs during this step's math, and the one
+// barrier per step both publishes the copy and retires the other stage.
 #include <type_traits>
 
 #include "common.h"
@@ -34,17 +39,60 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kThreads = 256;
+using S0 = std::integral_constant<int, 0>;
+using S1 = std::integral_constant<int, 1>;
+
 // k_bwd_kv
-constexpr int kKvBN = 128;         // key rows per workgroup
-constexpr int kKvBM = 32;          // query rows per step (half a row block)
-constexpr int kQStr = kD + 8;      // LDS row stride of the Q / dO tiles (bf16)
+constexpr int kKvBN = 128;                    // key rows per workgroup
+constexpr int kKvBM = 32;                     // query rows per step (half a row block)
+constexpr int kQStr = kD + 8;                 // LDS row stride of Q / dO (bf16): 272 B
+constexpr int kQSlots = kQStr * 2 / 16;       // 17 DMA slots per row
+constexpr int kQInstr = (kKvBM * kQSlots + 63) / 64;  // 9 wave DMA instructions per tile
+constexpr int kQStage = kQInstr * 512;        // bf16 elements per stage (whole instructions)
+constexpr int kStepWin = 2 * kListWin;        // steps per list window (two per row block)
+
 // k_bwd_q
-constexpr int kQBM = 128;          // query rows per workgroup
-constexpr int kQBN = 64;           // key columns per tile
-constexpr int kKStr = kD + 8;      // LDS row stride of K / V tiles (bf16)
+constexpr int kQBM = 128;                     // query rows per workgroup
+constexpr int kQBN = 64;                      // key columns per tile
+constexpr int kKStr = kD + 8;                 // LDS row stride of K / V (bf16): 272 B
+constexpr int kKSlots = kKStr * 2 / 16;       // 17
+constexpr int kKInstr = kQBN * kKSlots / 64;  // 17
+constexpr int kKStage = kKInstr * 512;
+static_assert(kQBN * kKSlots % 64 == 0, "whole DMA instructions");
 
 __device__ __forceinline__ bf16x8 concat4(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Wave-level: for the row blocks [w0, min(w0 + 64, nrb)) of a sequence of
+// length L, lists the 32-row steps (their first local row) of the blocks that
+// reach key columns [c0, c1): partly seen blocks into part, wholly seen ones
+// into full; returns the counts in every lane.
+__device__ __forceinline__ void step_window(const int4* env, int ni, int L, int nrb, int w0,
+                                            int c0, int c1, int* part, int* full_list,
+                                            int& n_part, int& n_full) {
+  const int lane = threadIdx.x & 63;
+  const int rb = w0 + lane;
+  bool live = false, full = false;
+  if (rb < nrb) block_vs_cols(env + (int64_t)rb * ni, ni, c0, c1, live, full);
+  full = full && live;
+  const bool partial = live && !full;
+  const bool second = rb * kRB + kKvBM < L;  // the block has a second 32-row step
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint64_t mp = __ballot(partial), mp2 = __ballot(partial && second);
+  const uint64_t mf = __ballot(full), mf2 = __ballot(full && second);
+  if (partial) {
+    const int pos = __popcll(mp & below) + __popcll(mp2 & below);
+    part[pos] = rb * kRB;
+    if (second) part[pos + 1] = rb * kRB + kKvBM;
+  }
+  if (full) {
+    const int pos = __popcll(mf & below) + __popcll(mf2 & below);
+    full_list[pos] = rb * kRB;
+    if (second) full_list[pos + 1] = rb * kRB + kKvBM;
+  }
+  n_part = __popcll(mp) + __popcll(mp2);
+  n_full = __popcll(mf) + __popcll(mf2);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
@@ -53,9 +101,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     uint16_t* __restrict__ dv, Prep P, const int4* __restrict__ units,
     const int* __restrict__ unit_count, int H, const int32_t* __restrict__ func, int nfunc,
     float alpha, float out_scale) {
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kKvBM * kQStr];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[kKvBM * kQStr];  // dO tile
+  // two LDS stages as separate objects, so the compiler sees that the DMA
+  // filling one stage does not alias the reads of the other
+  __shared__ __attribute__((aligned(16))) uint16_t sQ0[kQStage], sQ1[kQStage];
+  __shared__ __attribute__((aligned(16))) uint16_t sG0[kQStage], sG1[kQStage];  // dO
   __shared__ __attribute__((aligned(16))) uint32_t sMask[4][kKvBM];
+  __shared__ int sPart[kStepWin], sFull[kStepWin];
+  __shared__ int sCount[2];
 
   const int slot = xcd_slot(blockIdx.x, *unit_count);
   if (slot < 0) return;
@@ -93,20 +145,60 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     dvacc[mb] = f32x16{};
   }
 
-  // staging: thread loads rows lrow and lrow + 16 of the 32-row step, dims lcol..+7
-  const int lrow = tid >> 4, lcol = (tid & 15) * 8;
-  const int voff = lrow * rs2 + lcol * 2;
   const uint16_t* qh = q + s * rs + (int64_t)h * kD;
   const uint16_t* gh = dout + s * rs + (int64_t)h * kD;
+  // DMA of one 32-row step: wave w issues instructions I = w + 4i (I < 9) of
+  // each tensor; lane l of instruction I fills LDS slot 64*I + l
+  constexpr int kDmaPerWave = (kQInstr + 3) / 4;
+  int doff[kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int sl = (wave + 4 * i) * 64 + lane;
+    doff[i] = sl < kKvBM * kQSlots ? dma_slot_offset(sl, kQSlots, rs2) : kDmaSkip;
+  }
+  auto dma_step = [&](int q0, auto stage) {
+    constexpr int st = decltype(stage)::value;
+    const int rows = min(kKvBM, L - q0);
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qh + (int64_t)q0 * rs, rows, rs2, kD * 2);
+    const __amdgpu_buffer_rsrc_t rg = rows_rsrc(gh + (int64_t)q0 * rs, rows, rs2, kD * 2);
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int I = wave + 4 * i;
+      if (I < kQInstr) {
+        lds_dma16(rq, (st ? sQ1 : sQ0) + I * 512, doff[i]);
+        lds_dma16(rg, (st ? sG1 : sG0) + I * 512, doff[i]);
+      }
+    }
+  };
+
   // transpose-read base: lane j of 16-lane group G -> row 4*(G/2) + j/4,
   // column (G%2)*16 + 4*(j%4)
   const int grp = lane >> 4, gl = lane & 15;
   const int tr_off = (4 * (grp >> 1) + (gl >> 2)) * kQStr + (grp & 1) * 16 + 4 * (gl & 3);
   const int rd_off = n * kQStr + g * 8;
+  const int32_t* fseq = func + s;
 
-  // one 32-row step: rows q0..q0+31 staged in sQ / sG
-  auto step = [&](auto masked) {
+  // one 32-row step from LDS stage `stage`; `next` (>= 0) is the next step's
+  // first row, whose DMA is issued after this step's func loads
+  auto step = [&](int q0, int next, auto masked, auto stage) {
     constexpr bool kMasked = decltype(masked)::value;
+    constexpr int st = decltype(stage)::value;
+    const uint16_t* sQ = st ? sQ1 : sQ0;
+    const uint16_t* sG = st ? sG1 : sG0;
+    int lo[kMaxNI], hi[kMaxNI];
+    if constexpr (kMasked) row_intervals_rsrc(fseq, P.total, q0 + n, ni, L, lo, hi);
+    if (next >= 0) {
+      if constexpr (st == 0) {
+        dma_step(next, S1{});
+      } else {
+        dma_step(next, S0{});
+      }
+    }
+    if constexpr (kMasked) {
+      // row q0 + n: visibility of this wave's 32 key columns (wave-private
+      // LDS), built before the MFMAs so the intervals are dead during them
+      if (g == 0) sMask[wave][n] = col_mask32(lo, hi, ni, c0 + wave * 32);
+    }
     f32x16 sacc = f32x16{}, dsacc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) {
@@ -155,50 +247,37 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     }
   };
 
+  auto walk = [&](const int* list, int cnt, auto masked) {
+    if (cnt == 0) return;
+    dma_step(list[0], S0{});
+    for (int i = 0; i < cnt; i += 2) {
+      __syncthreads();
+      step(list[i], i + 1 < cnt ? list[i + 1] : -1, masked, S0{});
+      if (i + 1 >= cnt) break;
+      __syncthreads();
+      step(list[i + 1], i + 2 < cnt ? list[i + 2] : -1, masked, S1{});
+    }
+    __syncthreads();
+  };
+
   const int nrb = (L + kRB - 1) / kRB;
   const int4* env = P.env + (int64_t)P.rb_off[b] * ni;
-  // two passes over the row blocks that reach these keys: first those some
-  // rows see only partly (per-element mask), then those every row sees whole
-  auto pass = [&](auto masked) {
-    constexpr bool kMasked = decltype(masked)::value;
-    for (int rb = 0; rb < nrb; ++rb) {
-      bool live, full;
-      block_vs_cols(env + (int64_t)rb * ni, ni, c0, c1, live, full);
-      if (!live || full == kMasked) continue;
-      for (int half = 0; half < kRB / kKvBM; ++half) {
-        const int q0 = rb * kRB + half * kKvBM;
-        if (q0 >= L) break;
-        const int rows = min(kKvBM, L - q0);
-        const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qh + (int64_t)q0 * rs, rows, rs2, kD * 2);
-        const __amdgpu_buffer_rsrc_t rg = rows_rsrc(gh + (int64_t)q0 * rs, rows, rs2, kD * 2);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint4 a = buf_load16(rq, voff + 16 * i * rs2);
-          const uint4 c = buf_load16(rg, voff + 16 * i * rs2);
-          *reinterpret_cast<uint4*>(&sQ[(lrow + 16 * i) * kQStr + lcol]) = a;
-          *reinterpret_cast<uint4*>(&sG[(lrow + 16 * i) * kQStr + lcol]) = c;
-        }
-        if constexpr (kMasked) {
-          if (lane < kKvBM) {
-            // row q0 + lane: visibility of this wave's 32 key columns
-            int lo[kMaxNI], hi[kMaxNI];
-#pragma unroll
-            for (int j = 0; j < kMaxNI; ++j) {
-              lo[j] = L;
-              hi[j] = 0;
-              if (j < ni) row_interval_rsrc(func + s, P.total, q0 + lane, j, L, lo[j], hi[j]);
-            }
-            sMask[wave][lane] = col_mask32(lo, hi, ni, c0 + wave * 32);
-          }
-        }
-        __syncthreads();
-        step(masked);
-        __syncthreads();
+  for (int w0 = 0; w0 < nrb; w0 += kListWin) {
+    if (wave == 0) {
+      int np, nf;
+      step_window(env, ni, L, nrb, w0, c0, c1, sPart, sFull, np, nf);
+      if (lane == 0) {
+        sCount[0] = np;
+        sCount[1] = nf;
       }
     }
-  };
-  pass(std::true_type{});
-  pass(std::false_type{});
+    __syncthreads();
+    const int n_part = sCount[0], n_full = sCount[1];
+    walk(sPart, n_part, std::true_type{});
+    walk(sFull, n_full, std::false_type{});
+    // the next window rewrites the lists and counts: every wave is done with them
+    __syncthreads();
+  }
 
   // epilogue: lane holds d = mb*32 + j*8 + g*4 + 0..3 of key row `col`
   if (col_ok) {
@@ -226,8 +305,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
     Prep P, const int4* __restrict__ units, const int* __restrict__ unit_count, int H,
     const int32_t* __restrict__ func, int nfunc, float alpha, float out_scale) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kQBN * kKStr];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kQBN * kKStr];
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[kKStage], sK1[kKStage];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[kKStage], sV1[kKStage];
   __shared__ int sPart[kListWin], sFull[kListWin];
   __shared__ int sCount[2];
   __shared__ Envelope sEnv;
@@ -277,13 +356,35 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
 
   const uint16_t* kh = k + s * rs + (int64_t)h * kD;
   const uint16_t* vh = v + s * rs + (int64_t)h * kD;
-  const int krow = tid >> 4, kcol = (tid & 15) * 8;
-  const int voff = krow * rs2 + kcol * 2;
+  constexpr int kDmaPerWave = (kKInstr + 3) / 4;
+  int doff[kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i)
+    doff[i] = dma_slot_offset((wave + 4 * i) * 64 + lane, kKSlots, rs2);
+  auto dma_tile = [&](int t, auto stage) {
+    constexpr int st = decltype(stage)::value;
+    const int c0 = t * kQBN;
+    const int rows = min(kQBN, L - c0);
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kh + (int64_t)c0 * rs, rows, rs2, kD * 2);
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vh + (int64_t)c0 * rs, rows, rs2, kD * 2);
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int I = wave + 4 * i;
+      if (I < kKInstr) {
+        lds_dma16(rk, (st ? sK1 : sK0) + I * 512, doff[i]);
+        lds_dma16(rv, (st ? sV1 : sV0) + I * 512, doff[i]);
+      }
+    }
+  };
+
   const int grp = lane >> 4, gl = lane & 15;
   const int tr_off = (4 * (grp >> 1) + (gl >> 2)) * kKStr + (grp & 1) * 16 + 4 * (gl & 3);
 
-  auto compute = [&](int c0, auto masked) {
+  auto compute = [&](int c0, auto masked, auto stage) {
     constexpr bool kMasked = decltype(masked)::value;
+    constexpr int st = decltype(stage)::value;
+    const uint16_t* sK = st ? sK1 : sK0;
+    const uint16_t* sV = st ? sV1 : sV0;
     f32x16 sacc[2], dsacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -330,22 +431,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
   };
 
   auto walk = [&](const int* list, int cnt, auto masked) {
-    for (int i = 0; i < cnt; ++i) {
-      const int c0 = list[i] * kQBN;
-      const int rows = min(kQBN, L - c0);
-      const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kh + (int64_t)c0 * rs, rows, rs2, kD * 2);
-      const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vh + (int64_t)c0 * rs, rows, rs2, kD * 2);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const uint4 a = buf_load16(rk, voff + 16 * ii * rs2);
-        const uint4 c = buf_load16(rv, voff + 16 * ii * rs2);
-        *reinterpret_cast<uint4*>(&sK[(krow + 16 * ii) * kKStr + kcol]) = a;
-        *reinterpret_cast<uint4*>(&sV[(krow + 16 * ii) * kKStr + kcol]) = c;
-      }
+    if (cnt == 0) return;
+    dma_tile(list[0], S0{});
+    for (int i = 0; i < cnt; i += 2) {
       __syncthreads();
-      compute(c0, masked);
+      if (i + 1 < cnt) dma_tile(list[i + 1], S1{});
+      compute(list[i] * kQBN, masked, S0{});
+      if (i + 1 >= cnt) break;
       __syncthreads();
+      if (i + 2 < cnt) dma_tile(list[i + 2], S0{});
+      compute(list[i + 1] * kQBN, masked, S1{});
     }
+    __syncthreads();
   };
 
   for (int w0 = t_begin; w0 < t_end; w0 += kListWin) {
@@ -358,8 +455,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
       }
     }
     __syncthreads();
-    walk(sPart, sCount[0], std::true_type{});
-    walk(sFull, sCount[1], std::false_type{});
+    const int n_part = sCount[0], n_full = sCount[1];
+    walk(sPart, n_part, std::true_type{});
+    walk(sFull, n_full, std::false_type{});
+    // the next window rewrites the lists and counts: every wave is done with them
+    __syncthreads();
   }
 
   if (row_ok) {

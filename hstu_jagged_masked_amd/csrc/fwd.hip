@@ -7,9 +7,10 @@
 // owns rows [32w, 32w+32) of the tile.  Wave 0 lists, 64 tiles at a time, the
 // key tiles of 64 columns that the rows' interval envelopes reach (the rest are
 // never loaded) and flags the tiles every row sees whole.  For each listed tile:
-//   1. K and V tiles -> LDS, both row-major, through registers so the next
-//      tile's global loads overlap this tile's math; buffer loads whose range
-//      check zero-fills rows past the sequence end;
+//   1. K and V tiles -> LDS, both row-major, by asynchronous buffer-to-LDS
+//      DMA into one of two stages, so the next tile's copy runs during this
+//      tile's math (one barrier per tile); the buffer range check zero-fills
+//      rows past the sequence end;
 //   2. S^T = K Q^T on MFMA: A = K from LDS, B = Q^T from registers (each lane
 //      keeps its query row's 128 dims), so the accumulator holds one query row
 //      per lane and 16 key columns;
@@ -36,14 +37,25 @@ constexpr int kBN = 64;              // key columns per tile
 constexpr int kKStr = kD + 8;        // LDS row stride of K (bf16): 272 B, b128 reads conflict-free
 constexpr int kVStr = kD + 32;       // LDS row stride of V (bf16): 320 B, transpose reads conflict-free
 constexpr int kThreads = 256;
+constexpr int kKStage = kBN * kKStr;         // bf16 elements per K stage
+constexpr int kVStage = kBN * kVStr;
+constexpr int kKSlots = kKStr * 2 / 16;      // 16-byte DMA slots per LDS row
+constexpr int kVSlots = kVStr * 2 / 16;
+constexpr int kKInstr = kBN * kKSlots / 64;  // wave DMA instructions per stage
+constexpr int kVInstr = kBN * kVSlots / 64;
+constexpr int kDmaPerWave = (kVInstr + 3) / 4;
+static_assert(kBN * kKSlots % 64 == 0 && kBN * kVSlots % 64 == 0, "whole DMA instructions");
+static_assert(kKInstr <= 4 * kDmaPerWave && kVInstr <= 4 * kDmaPerWave, "DMA split");
 
 __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, Prep P, const int4* __restrict__ units,
     const int* __restrict__ unit_count, int H, const int32_t* __restrict__ func, int nfunc,
     float alpha, float out_scale) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBN * kKStr];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kBN * kVStr];
+  // two LDS stages as separate objects, so the compiler sees that the DMA
+  // filling one stage does not alias the reads of the other
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[kKStage], sK1[kKStage];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[kVStage], sV1[kVStage];
   __shared__ int sPart[kListWin], sFull[kListWin];
   __shared__ int sCount[2];
   __shared__ Envelope sEnv;
@@ -93,37 +105,39 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
   const uint16_t* kh = k + s * rs + (int64_t)h * kD;
   const uint16_t* vh = v + s * rs + (int64_t)h * kD;
 
-  // staging: thread loads rows krow + 16i, dims kcol..kcol+7, of K and V
-  const int krow = tid >> 4, kcol = (tid & 15) * 8;
-  const int voff = krow * rs2 + kcol * 2;
-  uint4 kreg[4], vreg[4];
-  auto load_tile = [&](int t) {
+  // DMA: wave w issues instructions I = w + 4i of a stage; lane l of
+  // instruction I fills LDS slot 64*I + l (padding slots read out of range)
+  int koff[kDmaPerWave], voff[kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int slot = (wave + 4 * i) * 64 + lane;
+    koff[i] = dma_slot_offset(slot, kKSlots, rs2);
+    voff[i] = dma_slot_offset(slot, kVSlots, rs2);
+  }
+  auto dma_tile = [&](int t, auto stage) {
+    constexpr int st = decltype(stage)::value;
     const int c0 = t * kBN;
     const int rows = min(kBN, L - c0);
     const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kh + (int64_t)c0 * rs, rows, rs2, kD * 2);
     const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vh + (int64_t)c0 * rs, rows, rs2, kD * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kreg[i] = buf_load16(rk, voff + 16 * i * rs2);
-      vreg[i] = buf_load16(rv, voff + 16 * i * rs2);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(&sK[(krow + 16 * i) * kKStr + kcol]) = kreg[i];
-      *reinterpret_cast<uint4*>(&sV[(krow + 16 * i) * kVStr + kcol]) = vreg[i];
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int I = wave + 4 * i;
+      if (I < kKInstr) lds_dma16(rk, (st ? sK1 : sK0) + I * 512, koff[i]);
+      if (I < kVInstr) lds_dma16(rv, (st ? sV1 : sV0) + I * 512, voff[i]);
     }
   };
   // transpose-read addressing for the A operand V^T: lane j of each 16-lane
   // group points at row j/4 of a 4-row block, columns 4*(j%4)..+3
   const int grp = lane >> 4, gl = lane & 15;
-  const uint16_t* vbase = &sV[(4 * (grp >> 1) + (gl >> 2)) * kVStr + (grp & 1) * 16 + 4 * (gl & 3)];
-  const uint16_t* kbase = &sK[n * kKStr + g * 8];
+  const int vrd = (4 * (grp >> 1) + (gl >> 2)) * kVStr + (grp & 1) * 16 + 4 * (gl & 3);
+  const int krd = n * kKStr + g * 8;
 
-  // one tile: S^T, SiLU (+ mask), O^T += V^T Y^T
-  auto compute = [&](int c0, auto masked) {
+  // one tile in LDS stage `stage`: S^T, SiLU (+ mask), O^T += V^T Y^T
+  auto compute = [&](int c0, auto masked, auto stage) {
     constexpr bool kMasked = decltype(masked)::value;
+    const uint16_t* kbase = (decltype(stage)::value ? sK1 : sK0) + krd;
+    const uint16_t* vbase = (decltype(stage)::value ? sV1 : sV0) + vrd;
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -165,20 +179,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
     }
   };
 
-  // walk a list of tiles: the next tile's loads are in flight while this one
-  // is computed
+  // walk a list of tiles, two LDS stages: the next tile's DMA runs while
+  // this tile is computed; the barrier before each tile both publishes its
+  // DMA (the barrier waits for outstanding memory operations) and retires the
+  // stage the new DMA overwrites
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
   auto walk = [&](const int* list, int cnt, auto masked) {
     if (cnt == 0) return;
-    load_tile(list[0]);
-    store_tile();
-    __syncthreads();
-    for (int i = 0; i < cnt; ++i) {
-      if (i + 1 < cnt) load_tile(list[i + 1]);
-      compute(list[i] * kBN, masked);
+    dma_tile(list[0], S0{});
+    for (int i = 0; i < cnt; i += 2) {
       __syncthreads();
-      if (i + 1 < cnt) store_tile();
+      if (i + 1 < cnt) dma_tile(list[i + 1], S1{});
+      compute(list[i] * kBN, masked, S0{});
+      if (i + 1 >= cnt) break;
       __syncthreads();
+      if (i + 2 < cnt) dma_tile(list[i + 2], S0{});
+      compute(list[i + 1] * kBN, masked, S1{});
     }
+    __syncthreads();
   };
 
   for (int w0 = t_begin; w0 < t_end; w0 += kListWin) {
@@ -191,8 +210,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
       }
     }
     __syncthreads();
-    walk(sPart, sCount[0], std::true_type{});
-    walk(sFull, sCount[1], std::false_type{});
+    const int n_part = sCount[0], n_full = sCount[1];
+    walk(sPart, n_part, std::true_type{});
+    walk(sFull, n_full, std::false_type{});
+    // the next window rewrites the lists and counts: every wave is done with them
+    __syncthreads();
   }
 
   // epilogue: lane holds O[row][mb*32 + j*8 + g*4 + 0..3]

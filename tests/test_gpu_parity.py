@@ -162,6 +162,15 @@ def test_bf16_sla_padded_bitwise(hj):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("mask", ["causal", "sla"])
+def test_bf16_long_sequences_several_list_windows(hj, mask):
+    """Sequences past 64 row blocks / key tiles (4096 rows): the kernels walk
+    their tile lists in several windows of 64 blocks."""
+    ls = np.array([4700, 130, 4160])
+    f = wl.func_causal(ls, 5) if mask == "causal" else wl.func_sla(ls, 1200, 32, 5)
+    run_case(hj, ls, 1, 128, "bf16", f, 1 / np.sqrt(128), 4700, seed=21)
+
+
 def test_bf16_three_interval(hj):
     ls = np.array([300, 520, 270, 100])
     run_case(hj, ls, 2, 128, "bf16", wl.func_three_interval(ls, 32, 8, 5), 1 / np.sqrt(128),
