@@ -45,20 +45,15 @@ using S1 = std::integral_constant<int, 1>;
 // k_bwd_kv
 constexpr int kKvBN = 128;                    // key rows per workgroup
 constexpr int kKvBM = 32;                     // query rows per step (half a row block)
-constexpr int kQStr = kD + 8;                 // LDS row stride of Q / dO (bf16): 272 B
-constexpr int kQSlots = kQStr * 2 / 16;       // 17 DMA slots per row
-constexpr int kQInstr = (kKvBM * kQSlots + 63) / 64;  // 9 wave DMA instructions per tile
-constexpr int kQStage = kQInstr * 512;        // bf16 elements per stage (whole instructions)
+constexpr int kQStage = kKvBM * kD;           // bf16 elements per swizzled stage (8 KiB)
+constexpr int kQInstr = kQStage / 512;        // 8 wave DMA instructions per tile
 constexpr int kStepWin = 2 * kListWin;        // steps per list window (two per row block)
 
 // k_bwd_q
 constexpr int kQBM = 128;                     // query rows per workgroup
 constexpr int kQBN = 64;                      // key columns per tile
-constexpr int kKStr = kD + 8;                 // LDS row stride of K / V (bf16): 272 B
-constexpr int kKSlots = kKStr * 2 / 16;       // 17
-constexpr int kKInstr = kQBN * kKSlots / 64;  // 17
-constexpr int kKStage = kKInstr * 512;
-static_assert(kQBN * kKSlots % 64 == 0, "whole DMA instructions");
+constexpr int kKStage = kQBN * kD;            // bf16 elements per swizzled stage (16 KiB)
+constexpr int kKInstr = kKStage / 512;        // 16 wave DMA instructions per tile
 
 __device__ __forceinline__ bf16x8 concat4(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -103,8 +98,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     float alpha, float out_scale) {
   // two LDS stages as separate objects, so the compiler sees that the DMA
   // filling one stage does not alias the reads of the other
-  __shared__ __attribute__((aligned(16))) uint16_t sQ0[kQStage], sQ1[kQStage];
-  __shared__ __attribute__((aligned(16))) uint16_t sG0[kQStage], sG1[kQStage];  // dO
+  __shared__ __attribute__((aligned(256))) uint16_t sQ0[kQStage], sQ1[kQStage];
+  __shared__ __attribute__((aligned(256))) uint16_t sG0[kQStage], sG1[kQStage];  // dO
   __shared__ __attribute__((aligned(16))) uint32_t sMask[4][kKvBM];
   __shared__ int sPart[kStepWin], sFull[kStepWin];
   __shared__ int sCount[2];
@@ -147,15 +142,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
 
   const uint16_t* qh = q + s * rs + (int64_t)h * kD;
   const uint16_t* gh = dout + s * rs + (int64_t)h * kD;
-  // DMA of one 32-row step: wave w issues instructions I = w + 4i (I < 9) of
-  // each tensor; lane l of instruction I fills LDS slot 64*I + l
-  constexpr int kDmaPerWave = (kQInstr + 3) / 4;
+  // DMA of one 32-row step: wave w issues instructions I = w + 4i of each
+  // tensor; lane l of instruction I fills LDS slot 64*I + l
+  constexpr int kDmaPerWave = kQInstr / 4;
   int doff[kDmaPerWave];
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const int sl = (wave + 4 * i) * 64 + lane;
-    doff[i] = sl < kKvBM * kQSlots ? dma_slot_offset(sl, kQSlots, rs2) : kDmaSkip;
-  }
+  for (int i = 0; i < kDmaPerWave; ++i) doff[i] = swz_dma_offset((wave + 4 * i) * 64 + lane, rs2);
   auto dma_step = [&](int q0, auto stage) {
     constexpr int st = decltype(stage)::value;
     const int rows = min(kKvBM, L - q0);
@@ -164,18 +156,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
       const int I = wave + 4 * i;
-      if (I < kQInstr) {
-        lds_dma16(rq, (st ? sQ1 : sQ0) + I * 512, doff[i]);
-        lds_dma16(rg, (st ? sG1 : sG0) + I * 512, doff[i]);
-      }
+      lds_dma16(rq, (st ? sQ1 : sQ0) + I * 512, doff[i]);
+      lds_dma16(rg, (st ? sG1 : sG0) + I * 512, doff[i]);
     }
   };
 
-  // transpose-read base: lane j of 16-lane group G -> row 4*(G/2) + j/4,
-  // column (G%2)*16 + 4*(j%4)
+  // Byte offsets into a swizzled tile.  Row reads: lane (n, g) reads row n
+  // (+ 32 kb), chunk 2 ks + g, at rd_b ^ 32 ks.  Transpose reads: lane j of
+  // 16-lane group G reads row 4*(G/2) + j/4 (+ 16 per slab), column
+  // (G%2)*16 + 4*(j%4) + 32 mb at tr_b ^ 64 mb, and the same rows + 8 at
+  // tr_b ^ 64 mb ^ 32 + 2 KiB.  The XORs are applied at each read so only two
+  // offsets stay live.
   const int grp = lane >> 4, gl = lane & 15;
-  const int tr_off = (4 * (grp >> 1) + (gl >> 2)) * kQStr + (grp & 1) * 16 + 4 * (gl & 3);
-  const int rd_off = n * kQStr + g * 8;
+  const int trow = 4 * (grp >> 1) + (gl >> 2);
+  const int rd_b0 = n * 256 + ((g ^ swz(n)) << 4);
+  const int tr_b0 = trow * 256 + 8 * (gl & 1) +
+                    ((((grp & 1) * 2 + ((gl & 3) >> 1)) ^ swz(trow)) << 4);
   const int32_t* fseq = func + s;
 
   // one 32-row step from LDS stage `stage`; `next` (>= 0) is the next step's
@@ -185,6 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     constexpr int st = decltype(stage)::value;
     const uint16_t* sQ = st ? sQ1 : sQ0;
     const uint16_t* sG = st ? sG1 : sG0;
+    const int rd_b = opaque(rd_b0), tr_b = opaque(tr_b0);
     int lo[kMaxNI], hi[kMaxNI];
     if constexpr (kMasked) row_intervals_rsrc(fseq, P.total, q0 + n, ni, L, lo, hi);
     if (next >= 0) {
@@ -202,10 +199,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     f32x16 sacc = f32x16{}, dsacc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) {
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8*>(&sQ[rd_off + ks * 16]), kf[ks], sacc, 0, 0, 0);
-      dsacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8*>(&sG[rd_off + ks * 16]), vf[ks], dsacc, 0, 0, 0);
+      const int off = rd_b ^ (32 * ks);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row16(sQ, off), kf[ks], sacc, 0, 0, 0);
+      dsacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row16(sG, off), vf[ks], dsacc, 0, 0, 0);
     }
     // element r: query row (r/4)*8 + g*4 + r%4 of the step, key column `col`
     bf16x8 yb[2], pb[2];
@@ -238,10 +234,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
       for (int mb = 0; mb < kD / 32; ++mb) {
-        const int off = tr_off + 16 * hh * kQStr + mb * 32;
-        const bf16x8 ag = concat4(lds_read_tr(&sG[off]), lds_read_tr(&sG[off + 8 * kQStr]));
+        const int o0 = (tr_b ^ (64 * mb)) + 16 * hh * 256;
+        const int o1 = (tr_b ^ (64 * mb) ^ 32) + (16 * hh + 8) * 256;
+        const bf16x8 ag = concat4(lds_tr8(sG, o0), lds_tr8(sG, o1));
         dvacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, yb[hh], dvacc[mb], 0, 0, 0);
-        const bf16x8 aq = concat4(lds_read_tr(&sQ[off]), lds_read_tr(&sQ[off + 8 * kQStr]));
+        const bf16x8 aq = concat4(lds_tr8(sQ, o0), lds_tr8(sQ, o1));
         dkacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, pb[hh], dkacc[mb], 0, 0, 0);
       }
     }
@@ -251,10 +248,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     if (cnt == 0) return;
     dma_step(list[0], S0{});
     for (int i = 0; i < cnt; i += 2) {
-      __syncthreads();
+      dma_barrier();
       step(list[i], i + 1 < cnt ? list[i + 1] : -1, masked, S0{});
       if (i + 1 >= cnt) break;
-      __syncthreads();
+      dma_barrier();
       step(list[i + 1], i + 2 < cnt ? list[i + 2] : -1, masked, S1{});
     }
     __syncthreads();
@@ -305,8 +302,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
     Prep P, const int4* __restrict__ units, const int* __restrict__ unit_count, int H,
     const int32_t* __restrict__ func, int nfunc, float alpha, float out_scale) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[kKStage], sK1[kKStage];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[kKStage], sV1[kKStage];
+  __shared__ __attribute__((aligned(256))) uint16_t sK0[kKStage], sK1[kKStage];
+  __shared__ __attribute__((aligned(256))) uint16_t sV0[kKStage], sV1[kKStage];
   __shared__ int sPart[kListWin], sFull[kListWin];
   __shared__ int sCount[2];
   __shared__ Envelope sEnv;
@@ -356,11 +353,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
 
   const uint16_t* kh = k + s * rs + (int64_t)h * kD;
   const uint16_t* vh = v + s * rs + (int64_t)h * kD;
-  constexpr int kDmaPerWave = (kKInstr + 3) / 4;
+  constexpr int kDmaPerWave = kKInstr / 4;
   int doff[kDmaPerWave];
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i)
-    doff[i] = dma_slot_offset((wave + 4 * i) * 64 + lane, kKSlots, rs2);
+  for (int i = 0; i < kDmaPerWave; ++i) doff[i] = swz_dma_offset((wave + 4 * i) * 64 + lane, rs2);
   auto dma_tile = [&](int t, auto stage) {
     constexpr int st = decltype(stage)::value;
     const int c0 = t * kQBN;
@@ -370,34 +366,41 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
       const int I = wave + 4 * i;
-      if (I < kKInstr) {
-        lds_dma16(rk, (st ? sK1 : sK0) + I * 512, doff[i]);
-        lds_dma16(rv, (st ? sV1 : sV0) + I * 512, doff[i]);
-      }
+      lds_dma16(rk, (st ? sK1 : sK0) + I * 512, doff[i]);
+      lds_dma16(rv, (st ? sV1 : sV0) + I * 512, doff[i]);
     }
   };
 
+  // Byte offsets into a swizzled tile.  Row reads: lane (n, g) reads row n
+  // (+ 32 kb), chunk 2 ks + g, at rd_b ^ 32 ks.  Transpose reads: lane j of
+  // 16-lane group G reads row 4*(G/2) + j/4 (+ 16 per slab), column
+  // (G%2)*16 + 4*(j%4) + 32 mb at tr_b ^ 64 mb, and the same rows + 8 at
+  // tr_b ^ 64 mb ^ 32 + 2 KiB.  The XORs are applied at each read so only two
+  // offsets stay live.
   const int grp = lane >> 4, gl = lane & 15;
-  const int tr_off = (4 * (grp >> 1) + (gl >> 2)) * kKStr + (grp & 1) * 16 + 4 * (gl & 3);
+  const int trow = 4 * (grp >> 1) + (gl >> 2);
+  const int rd_b0 = n * 256 + ((g ^ swz(n)) << 4);
+  const int tr_b0 = trow * 256 + 8 * (gl & 1) +
+                    ((((grp & 1) * 2 + ((gl & 3) >> 1)) ^ swz(trow)) << 4);
 
   auto compute = [&](int c0, auto masked, auto stage) {
     constexpr bool kMasked = decltype(masked)::value;
     constexpr int st = decltype(stage)::value;
     const uint16_t* sK = st ? sK1 : sK0;
     const uint16_t* sV = st ? sV1 : sV0;
+    const int rd_b = opaque(rd_b0), tr_b = opaque(tr_b0);
     f32x16 sacc[2], dsacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x16{};
       dsacc[kb] = f32x16{};
-      const uint16_t* kp = &sK[(kb * 32 + n) * kKStr + g * 8];
-      const uint16_t* vp = &sV[(kb * 32 + n) * kKStr + g * 8];
 #pragma unroll
       for (int ks = 0; ks < kD / 16; ++ks) {
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(kp + ks * 16), qf[ks], sacc[kb], 0, 0, 0);
-        dsacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(vp + ks * 16), gf[ks], dsacc[kb], 0, 0, 0);
+        const int off = (rd_b ^ (32 * ks)) + kb * 32 * 256;
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row16(sK, off), qf[ks], sacc[kb],
+                                                           0, 0, 0);
+        dsacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row16(sV, off), gf[ks],
+                                                            dsacc[kb], 0, 0, 0);
       }
     }
     bf16x8 pb[4];
@@ -423,8 +426,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
     for (int ss = 0; ss < 4; ++ss) {
 #pragma unroll
       for (int mb = 0; mb < kD / 32; ++mb) {
-        const int off = tr_off + 16 * ss * kKStr + mb * 32;
-        const bf16x8 a = concat4(lds_read_tr(&sK[off]), lds_read_tr(&sK[off + 8 * kKStr]));
+        const int o0 = (tr_b ^ (64 * mb)) + 16 * ss * 256;
+        const int o1 = (tr_b ^ (64 * mb) ^ 32) + (16 * ss + 8) * 256;
+        const bf16x8 a = concat4(lds_tr8(sK, o0), lds_tr8(sK, o1));
         dqacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ss], dqacc[mb], 0, 0, 0);
       }
     }
@@ -434,11 +438,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
     if (cnt == 0) return;
     dma_tile(list[0], S0{});
     for (int i = 0; i < cnt; i += 2) {
-      __syncthreads();
+      dma_barrier();
       if (i + 1 < cnt) dma_tile(list[i + 1], S1{});
       compute(list[i] * kQBN, masked, S0{});
       if (i + 1 >= cnt) break;
-      __syncthreads();
+      dma_barrier();
       if (i + 2 < cnt) dma_tile(list[i + 2], S0{});
       compute(list[i + 1] * kQBN, masked, S1{});
     }

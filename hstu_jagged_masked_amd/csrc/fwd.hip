@@ -189,11 +189,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
     if (cnt == 0) return;
     dma_tile(list[0], S0{});
     for (int i = 0; i < cnt; i += 2) {
-      __syncthreads();
+      dma_barrier();
       if (i + 1 < cnt) dma_tile(list[i + 1], S1{});
       compute(list[i] * kBN, masked, S0{});
       if (i + 1 >= cnt) break;
-      __syncthreads();
+      dma_barrier();
       if (i + 2 < cnt) dma_tile(list[i + 2], S0{});
       compute(list[i + 1] * kBN, masked, S1{});
     }

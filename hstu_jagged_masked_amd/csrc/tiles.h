@@ -177,6 +177,16 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, i
       r, (__attribute__((address_space(3))) void*)lds, 16, voffset, 0, 0, 0);
 }
 
+// Waits until every DMA this wave issued has landed in LDS, then joins the
+// workgroup barrier: afterwards every wave sees every wave's copied tiles.
+// The wait is explicit because the barrier's own lowering waits for LDS DMA
+// only when the compiler cannot prove that the next LDS reads miss it, which
+// says nothing about the reads of the other waves.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 // A voffset no buffer in this library reaches: its DMA lane writes zeros.
 constexpr int kDmaSkip = 0x7ff00000;
 
@@ -185,6 +195,44 @@ constexpr int kDmaSkip = 0x7ff00000;
 __device__ __forceinline__ int dma_slot_offset(int s, int chunks, int row_bytes) {
   const int r = s / chunks, c = s - r * chunks;
   return c < 16 ? r * row_bytes + c * 16 : kDmaSkip;
+}
+
+// Swizzled LDS tiles: 256-byte rows (one D = 128 bf16 row) of 16 16-byte
+// chunks, chunk c of row r stored at position c ^ swz(r).  Every 16
+// consecutive rows read at one chunk (the 16 lanes a b128 row read serves per
+// LDS cycle) and every 4 aligned consecutive rows read across an aligned quad
+// of chunks (the 32 lanes of a pair of transpose-read groups) land on 16
+// distinct positions, i.e. on all 64 banks once.  swz depends on r mod 16
+// only, and swz(r + 8) = swz(r) ^ 2.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// bf16 element index of (row r, column col) in a swizzled tile.
+__device__ __forceinline__ int swz_index(int r, int col) {
+  return r * 128 + ((((col >> 3) ^ swz(r))) << 3) + (col & 7);
+}
+
+// 16-byte row read and 8-byte transpose read (lds_read_tr) at a byte offset
+// into an LDS tile.
+__device__ __forceinline__ bf16x8 lds_row16(const uint16_t* tile, int byte_off) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + byte_off);
+}
+__device__ __forceinline__ bf16x4 lds_tr8(const uint16_t* tile, int byte_off) {
+  return lds_read_tr(reinterpret_cast<const uint16_t*>(
+      reinterpret_cast<const char*>(tile) + byte_off));
+}
+
+// The value of x, hidden from the optimiser: offsets derived from it inside a
+// loop are recomputed there instead of being hoisted into live registers.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Global byte offset that DMA slot s (LDS bytes [16 s, 16 s + 16)) of a
+// swizzled tile copies, for rows row_bytes apart.
+__device__ __forceinline__ int swz_dma_offset(int s, int row_bytes) {
+  const int r = s >> 4;
+  return r * row_bytes + (((s & 15) ^ swz(r)) << 4);
 }
 
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voffset) {

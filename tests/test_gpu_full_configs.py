@@ -63,13 +63,23 @@ def to64(x):
     return x.float().cpu().numpy().astype(np.float64)
 
 
-def run_full(hj, cfg, func_np, seqs, nfunc_label=""):
-    """fwd+bwd on the whole workload; oracle on the sequences `seqs`."""
+def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False):
+    """fwd+bwd on the whole workload; oracle on the sequences `seqs`.  With
+    `repeat`, a second fwd+bwd must reproduce every output bit for bit (each
+    output element is written by one workgroup in a fixed order, so any
+    difference is a race)."""
     t, off = device_inputs(cfg)
     func = torch.from_numpy(func_np).to(DEV)
     o = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], func, cfg["alpha"], cfg["max_len"])
     dq, dk, dv = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
                              cfg["max_len"])
+    if repeat:
+        o2 = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], func, cfg["alpha"], cfg["max_len"])
+        g2 = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
+                         cfg["max_len"])
+        for nm, a, b in zip(("o", "dq", "dk", "dv"), (o, dq, dk, dv), (o2,) + tuple(g2)):
+            assert torch.equal(a, b), f"{cfg['name']}.{nm}: second run differs"
+        del o2, g2
     torch.cuda.synchronize()
     rows, sub_off = oracle.subset(off, seqs)
     rows_t = torch.from_numpy(rows).to(DEV)
@@ -121,7 +131,7 @@ def test_hstu_layer_shapes_sampled(hj, name):
     cfg = wl.workload(name)
     ls = cfg["lengths"]
     f = cfg["func"](ls, 5)
-    run_full(hj, cfg, f, sample_seqs(ls))
+    run_full(hj, cfg, f, sample_seqs(ls), repeat=True)
     off_t = torch.from_numpy(wl.offsets_from_lengths(ls)).to(DEV)
     counts, tot = hj.visible_counts(off_t, torch.from_numpy(f).to(DEV), int(ls.sum()))
     assert np.array_equal(counts.cpu().numpy(), wl.local_rows(ls) + 1), "causal counts"
