@@ -37,7 +37,8 @@ METRIC = "HSTU attn fwd+bwd ms + effective TFLOP/s (% bf16 MFMA peak), B=1024 L=
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # algorithmic flops per visible pair and head, as multiples of D
-KERNEL_FLOPS_PER_PAIR = {"k_fwd_bf16": 4, "k_bwd_kv": 8, "k_bwd_q": 2}
+KERNEL_FLOPS_PER_PAIR = {"k_fwd_bf16": 4, "k_bwd_kv": 8, "k_bwd_kv_p": 8, "k_bwd_q": 2,
+                         "k_bwd_dq": 2}
 
 
 def log(msg):
@@ -85,15 +86,15 @@ def make_inputs(cfg, device, targets=False):
     return t, off
 
 
-def run_steps(hj, t, cfg, n, targets=False):
+def run_steps(hj, t, cfg, n, targets=False, pstore=None):
     tr = t.get("tr") if targets else None
     for _ in range(n):
         hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], t["func"], cfg["alpha"], cfg["max_len"], tr)
         hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], t["func"], cfg["alpha"],
-                    cfg["max_len"], tr)
+                    cfg["max_len"], tr, pstore=pstore)
 
 
-def timed(hj, torch, t, cfg, steps, targets=False):
+def timed(hj, torch, t, cfg, steps, targets=False, pstore=None):
     torch.cuda.synchronize()
     hj.profile_reset()
     hj.profile_enable(True)
@@ -101,7 +102,7 @@ def timed(hj, torch, t, cfg, steps, targets=False):
     e1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     e0.record()
-    run_steps(hj, t, cfg, steps, targets)
+    run_steps(hj, t, cfg, steps, targets, pstore)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -143,6 +144,10 @@ def main():
     ap.add_argument("--targets-steps", type=int, default=20)
     ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences in the CPU oracle sample (0 disables it)")
+    ap.add_argument("--dq", choices=("auto", "stored-p", "recompute"), default="auto",
+                    help="dQ path of the backward: from stored P (needs ~2 bytes per (row, "
+                         "column) pair of each sequence per head of HBM; 'auto' uses it when it "
+                         "fits) or recomputing the scores")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="size of a plain device-to-device copy run once before timing; "
                          "counter runs scale HBM byte counters by it (0 disables it)")
@@ -177,10 +182,17 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    run_steps(hj, t, cfg, args.warmup)
+    pstore = None
+    p_bytes = hj.pstore_bytes(t["off"], H)
+    free, _ = torch.cuda.mem_get_info(device)
+    use_p = args.dq == "stored-p" or (args.dq == "auto" and p_bytes + (16 << 30) < free)
+    if use_p:
+        pstore = torch.empty(p_bytes, dtype=torch.uint8, device=device)
+    log(f"[bench] dQ path: {'stored P, %.1f GB' % (p_bytes / 1e9) if use_p else 'recompute'}")
+    run_steps(hj, t, cfg, args.warmup, pstore=pstore)
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
-    ms, wall, prof = timed(hj, torch, t, cfg, args.steps)
+    ms, wall, prof = timed(hj, torch, t, cfg, args.steps, pstore=pstore)
     log(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step")
     flops_eff = 14.0 * D * H * pairs
     value = flops_eff / (ms * 1e-3) / 1e12
@@ -201,6 +213,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(dom)}
 
+    del pstore
     # targets-only mode on the same K/V
     tt, _ = make_inputs(cfg, device, targets=True)
     tt["k"], tt["v"] = t["k"], t["v"]
@@ -242,7 +255,9 @@ def main():
         "config": {"workload": args.workload, "batch": len(cfg["lengths"]),
                    "seq_len": int(cfg["lengths"].max()), "tokens": T, "heads": H, "head_dim": D,
                    "nfunc": cfg["nfunc"], "mask": "causal" if "hstu" in args.workload else
-                   args.workload, "visible_pairs_per_head": pairs},
+                   args.workload, "visible_pairs_per_head": pairs,
+                   "dq_path": "stored_p" if use_p else "recompute",
+                   "pstore_gb": round(p_bytes / 1e9, 2) if use_p else 0.0},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -9,7 +9,9 @@ library is missing the import of the op raises.
 Entry points mirror the C ABI (include/hstu_attn.h):
 
     attn_fwd(q, k, v, seq_offsets, func, alpha, max_len, target_rows=None) -> o
-    attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None) -> dq, dk, dv
+    attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None,
+             pstore=None) -> dq, dk, dv
+    pstore_bytes(seq_offsets, H) -> bytes of the stored-P buffer attn_bwd(pstore=...) needs
     visible_counts(seq_offsets, func, total, target_rows=None) -> (counts, total_pairs)
     check_inputs(seq_offsets, total, target_rows=None)
     hstu_attention(...)  # autograd.Function wrapper of the two above
@@ -70,6 +72,11 @@ def library() -> ctypes.CDLL:
     lib.hstu_attn_visible_counts.restype = i32
     lib.hstu_attn_check_inputs.argtypes = [P, i64, i64, P, P, sz, P]
     lib.hstu_attn_check_inputs.restype = i32
+    lib.hstu_attn_bwd_pstore.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i32, i32, P, i32, f32,
+                                         i64, P, sz, P, sz, P]
+    lib.hstu_attn_bwd_pstore.restype = i32
+    lib.hstu_attn_pstore_bytes.argtypes = [P, i64, i64, i32]
+    lib.hstu_attn_pstore_bytes.restype = sz
     lib.hstu_profile_enable.argtypes = [i32]
     lib.hstu_profile_enable.restype = i32
     lib.hstu_profile_read.argtypes = [ctypes.c_char_p, sz]
@@ -81,7 +88,8 @@ def library() -> ctypes.CDLL:
 
 
 EXPORTED = ("hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size", "hstu_attn_fwd",
-            "hstu_attn_bwd", "hstu_attn_visible_counts", "hstu_attn_check_inputs",
+            "hstu_attn_bwd", "hstu_attn_bwd_pstore", "hstu_attn_pstore_bytes",
+            "hstu_attn_visible_counts", "hstu_attn_check_inputs",
             "hstu_profile_enable", "hstu_profile_read", "hstu_profile_reset")
 
 
@@ -158,7 +166,20 @@ def attn_fwd(q, k, v, seq_offsets, func, alpha, max_len, target_rows=None, out=N
     return o
 
 
-def attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None):
+def pstore_bytes(seq_offsets, H) -> int:
+    """Bytes of the stored-P buffer for attn_bwd(pstore=...): the sum over
+    sequences of ceil(L/128) * ceil(L/32) * 8192 * H (reads the offsets back
+    to the host)."""
+    off = seq_offsets.detach().to("cpu", torch.int64).contiguous()
+    B = off.numel() - 1
+    total = int(off[-1].item()) if B >= 0 else 0
+    return int(library().hstu_attn_pstore_bytes(ctypes.c_void_p(off.data_ptr()), B, total, int(H)))
+
+
+def attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None, pstore=None):
+    """Backward.  With ``pstore`` (a CUDA uint8 tensor of at least
+    ``pstore_bytes(seq_offsets, H)`` bytes; bf16, D = 128, full-length mode) the
+    stored-P path runs: no recomputation of the scores for dQ."""
     B, total, H, D, nfunc = _common(q, k, seq_offsets, func, target_rows)
     for t in (q, k, v, dout):
         if not t.is_contiguous() or t.dtype != k.dtype:
@@ -169,6 +190,16 @@ def attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None)
     dv = torch.empty_like(v)
     ws_bytes = workspace_size(1, code, B, total, H, D, nfunc, target_rows is not None)
     ws = _workspace(ws_bytes, k.device)
+    if pstore is not None:
+        if target_rows is not None or code != HSTU_BF16:
+            raise ValueError("the stored-P backward needs bf16 and full-length mode")
+        if pstore.dtype != torch.uint8 or not pstore.is_contiguous():
+            raise ValueError("pstore must be a contiguous uint8 tensor")
+        _check(library().hstu_attn_bwd_pstore(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(seq_offsets), B, total, H, D, _ptr(func), nfunc, float(alpha), int(max_len),
+            _ptr(ws), ws.numel(), _ptr(pstore), pstore.numel(), _stream(k.device)))
+        return dq, dk, dv
     _check(library().hstu_attn_bwd(
         code, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(seq_offsets), B, total, H, D, _ptr(func), nfunc, float(alpha), int(max_len),

@@ -79,6 +79,7 @@ bool plan_workspace(Plan& p, int is_bwd, int dtype, int64_t B, int64_t total, in
     p.partial_bytes = (size_t)nchunk * H * D * sizeof(float);
   }
   p.off_partial = take(p.partial_bytes);
+  if (is_bwd && !targets_only) p.off_pblk = take((size_t)(B + 1) * sizeof(int64_t));
   p.bytes = off;
   return true;
 }
@@ -93,6 +94,7 @@ Prep prep_view(const Plan& p, void* ws, int B, int64_t total) {
   P.tiles64 = reinterpret_cast<int*>(base + p.off_t64);
   P.tiles128 = reinterpret_cast<int*>(base + p.off_t128);
   P.env = reinterpret_cast<int4*>(base + p.off_env);
+  P.pblk = p.off_pblk ? reinterpret_cast<int64_t*>(base + p.off_pblk) : nullptr;
   P.B = B;
   P.total = total;
   P.nrb_cap = p.nrb_cap;
@@ -245,11 +247,76 @@ extern "C" int hstu_attn_bwd(int dtype, const void* q, const void* k, const void
     if (e == hipSuccess) e = launch_units(P, Uq, 128, 1, H, kSlotQUnits, s);
     if (e != hipSuccess) return device_fail(e, "unit list");
     e = launch_mfma_bwd(q, k, v, dout, dq, dk, dv, P, Ukv, Uq, H, func, nfunc, alpha,
-                        inv_max_len, s);
+                        inv_max_len, nullptr, s);
   } else {
     e = launch_generic_bwd(dtype, D, q, k, v, dout, dq, dk, dv, P, H, func, nfunc, alpha,
                            inv_max_len, nullptr, s);
   }
+  if (e != hipSuccess) return device_fail(e, "backward");
+  return HSTU_OK;
+}
+
+extern "C" size_t hstu_attn_pstore_bytes(const int64_t* seq_offsets, int64_t B, int64_t total,
+                                         int H) {
+  if (!seq_offsets || B < 1 || B > (1 << 24) || total < 0 || total > (int64_t)INT32_MAX || H < 1 ||
+      H > 255)
+    return 0;
+  // the lengths the device sees: offsets clamped into [0, total], running
+  // maximum, first 0 and last `total`
+  int64_t blocks = 0, prev = 0, run = 0;
+  for (int64_t b = 1; b <= B; ++b) {
+    int64_t x = seq_offsets[b] < 0 ? 0 : (seq_offsets[b] > total ? total : seq_offsets[b]);
+    run = x > run ? x : run;
+    const int64_t cur = b == B ? total : run;
+    const int64_t L = cur - prev;
+    blocks += cdiv64(L, 128) * cdiv64(L, 32);
+    prev = cur;
+  }
+  return (size_t)blocks * H * 8192;
+}
+
+extern "C" int hstu_attn_bwd_pstore(const void* q, const void* k, const void* v, const void* dout,
+                                    void* dq, void* dk, void* dv, const int64_t* seq_offsets,
+                                    int64_t B, int64_t total, int H, int D, const int32_t* func,
+                                    int nfunc, float alpha, int64_t max_len, void* workspace,
+                                    size_t workspace_bytes, void* pstore, size_t pstore_bytes,
+                                    void* stream) {
+  Plan plan;
+  int st = validate(plan, 1, HSTU_BF16, B, total, H, D, nfunc, alpha, max_len, seq_offsets, func,
+                    nullptr, workspace, workspace_bytes);
+  if (st) return st;
+  if (D != 128)
+    return fail(HSTU_ERR_UNSUPPORTED, "the stored-P backward needs D = 128, got %d", D);
+  if ((st = check_tensor(q, total, "q")) || (st = check_tensor(k, total, "k")) ||
+      (st = check_tensor(v, total, "v")) || (st = check_tensor(dout, total, "dout")) ||
+      (st = check_tensor(dq, total, "dq")) || (st = check_tensor(dk, total, "dk")) ||
+      (st = check_tensor(dv, total, "dv")))
+    return st;
+  if (total > 0 && !pstore) return fail(HSTU_ERR_INVALID, "pstore is NULL");
+  if (reinterpret_cast<uintptr_t>(pstore) & 255u)
+    return fail(HSTU_ERR_INVALID, "pstore must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float inv_max_len = (float)(1.0 / (double)max_len);
+  Prep P = prep_view(plan, workspace, (int)B, total);
+  hipError_t e = launch_prep(P, seq_offsets, nullptr, func, nfunc, s);
+  if (e != hipSuccess) return device_fail(e, "prep");
+  // the stored-P size follows from the device's sanitized lengths: read it
+  // back and refuse a buffer that is too small before any kernel writes P
+  int64_t blocks = 0;
+  e = hipMemcpyAsync(&blocks, P.pblk + B, sizeof(int64_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return device_fail(e, "reading the stored-P size");
+  const size_t need = (size_t)blocks * H * 8192;
+  if (pstore_bytes < need)
+    return fail(HSTU_ERR_WORKSPACE, "stored-P buffer of %zu bytes given, %zu needed", pstore_bytes,
+                need);
+  Units Ukv = units_view(workspace, plan.off_units_b, plan.cap_b);
+  Units Uq = units_view(workspace, plan.off_units_c, plan.cap_c);
+  e = launch_units(P, Ukv, 128, 0, H, kSlotKvUnits, s);
+  if (e == hipSuccess) e = launch_units(P, Uq, 128, 1, H, kSlotQUnits, s);
+  if (e != hipSuccess) return device_fail(e, "unit list");
+  e = launch_mfma_bwd(q, k, v, dout, dq, dk, dv, P, Ukv, Uq, H, func, nfunc, alpha, inv_max_len,
+                      static_cast<uint16_t*>(pstore), s);
   if (e != hipSuccess) return device_fail(e, "backward");
   return HSTU_OK;
 }

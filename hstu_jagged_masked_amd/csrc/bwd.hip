@@ -90,12 +90,25 @@ __device__ __forceinline__ void step_window(const int4* env, int ni, int L, int 
   n_full = __popcll(mf) + __popcll(mf2);
 }
 
+// kStoreP: also store each step's P (bf16, as rounded for the dK product) for
+// the dQ pass.  Layout, per (sequence, head): blocks [128-key tile kt][32-row
+// step] of 8 KiB, block (kt, step) at ((pblk[b] H + h nkt nsteps) + kt nsteps
+// + step) * 8 KiB.  A block is the B operand of dQ^T += K^T P^T, ready to
+// load: [key step ks of 16 keys][lane l][8 bf16], lane l holding the keys
+// 16 ks + 8 (l/32) + 0..7 of row position l%32, where row position
+// hh*16 + g*8 + e is query row (2 hh + e/4)*8 + g*4 + e%4 of the step (the
+// order of the registers pb[hh][e] of lane (key, g)).  The transpose goes
+// through a wave-private LDS buffer, and a step's stores are issued at the
+// start of the next step so that they have landed by the barrier after it
+// (stores and loads share vmcnt).  Only the steps a key tile walks are
+// written; the dQ pass reads exactly those.
+template <bool kStoreP>
 __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, Prep P, const int4* __restrict__ units,
     const int* __restrict__ unit_count, int H, const int32_t* __restrict__ func, int nfunc,
-    float alpha, float out_scale) {
+    float alpha, float out_scale, uint16_t* __restrict__ pstore) {
   // two LDS stages as separate objects, so the compiler sees that the DMA
   // filling one stage does not alias the reads of the other
   __shared__ __attribute__((aligned(256))) uint16_t sQ0[kQStage], sQ1[kQStage];
@@ -103,6 +116,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   __shared__ __attribute__((aligned(16))) uint32_t sMask[4][kKvBM];
   __shared__ int sPart[kStepWin], sFull[kStepWin];
   __shared__ int sCount[2];
+  // P staging: per wave [32 keys][32 row positions], 64-byte rows
+  __shared__ __attribute__((aligned(16))) uint16_t sPst[kStoreP ? 4 * 1024 : 8];
 
   const int slot = xcd_slot(blockIdx.x, *unit_count);
   if (slot < 0) return;
@@ -142,6 +157,33 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
 
   const uint16_t* qh = q + s * rs + (int64_t)h * kD;
   const uint16_t* gh = dout + s * rs + (int64_t)h * kD;
+  // stored P: this workgroup's first block (uniform); the staged step
+  int64_t p_blk0 = 0;
+  int p_pending = -1;  // first row of the step whose P sits in sPst, or -1
+  if constexpr (kStoreP) {
+    const int64_t nkt = (L + kKvBN - 1) / kKvBN, nsteps = (L + kKvBM - 1) / kKvBM;
+    p_blk0 = uniform(P.pblk[b] * H + h * nkt * nsteps + kt * nsteps);
+  }
+  uint16_t* const p_stage = sPst + (kStoreP ? wave * 1024 : 0);
+  // transpose reads of the staging rows: lane j of 16-lane group G reads key
+  // row 8*(G/2) + j/4 (+ 16 ksl, + 4 for the second read), row positions
+  // (G%2)*16 + 4*(j%4)..+3; lane l then holds keys 16 ksl + 8 (l/32) + 0..7 of
+  // row position l%32
+  const int p_tr = (8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * 64 +
+                   (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+  auto p_flush = [&]() {
+    if constexpr (kStoreP) {
+      if (p_pending < 0) return;
+      uint16_t* blk = pstore + ((p_blk0 + p_pending / kKvBM) << 12) + lane * 8;
+#pragma unroll
+      for (int ksl = 0; ksl < 2; ++ksl) {
+        const bf16x8 t = concat4(lds_tr8(p_stage, p_tr + ksl * 16 * 64),
+                                 lds_tr8(p_stage, p_tr + (ksl * 16 + 4) * 64));
+        *reinterpret_cast<bf16x8*>(blk + (2 * wave + ksl) * 512) = t;
+      }
+      p_pending = -1;
+    }
+  };
   // DMA of one 32-row step: wave w issues instructions I = w + 4i of each
   // tensor; lane l of instruction I fills LDS slot 64*I + l
   constexpr int kDmaPerWave = kQInstr / 4;
@@ -196,6 +238,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
       // LDS), built before the MFMAs so the intervals are dead during them
       if (g == 0) sMask[wave][n] = col_mask32(lo, hi, ni, c0 + wave * 32);
     }
+    // the previous step's P (after the mask, whose func loads must not wait
+    // behind stores)
+    p_flush();
     f32x16 sacc = f32x16{}, dsacc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) {
@@ -227,6 +272,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
         yb[r >> 3][r & 7] = (__bf16)y;
         pb[r >> 3][r & 7] = (__bf16)p;
       }
+    }
+    if constexpr (kStoreP) {
+      // stage [key n][row position hh*16 + g*8 + e]; stored by the next step
+      *reinterpret_cast<bf16x8*>(p_stage + n * 32 + g * 8) = pb[0];
+      *reinterpret_cast<bf16x8*>(p_stage + n * 32 + 16 + g * 8) = pb[1];
+      p_pending = q0;
     }
     // dV^T += dO^T Y and dK^T += Q^T P: A operands by transpose reads, query
     // rows 16hh + 4g + {0..3} and 16hh + 8 + 4g + {0..3}
@@ -275,6 +326,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     // the next window rewrites the lists and counts: every wave is done with them
     __syncthreads();
   }
+  p_flush();
 
   // epilogue: lane holds d = mb*32 + j*8 + g*4 + 0..3 of key row `col`
   if (col_ok) {
@@ -486,18 +538,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
 hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const void* dout,
                            void* dq, void* dk, void* dv, const Prep& P, const Units& Ukv,
                            const Units& Uq, int H, const int32_t* func, int nfunc, float alpha,
-                           float inv_max_len, hipStream_t stream) {
+                           float inv_max_len, uint16_t* pstore, hipStream_t stream) {
   const float scale = alpha * inv_max_len;
   if (Ukv.cap > 0) {
-    ProfScope ps(stream, "k_bwd_kv");
-    hipLaunchKernelGGL(k_bwd_kv, dim3(Ukv.cap), dim3(kThreads), 0, stream,
+    ProfScope ps(stream, pstore ? "k_bwd_kv_p" : "k_bwd_kv");
+    auto kern = pstore ? k_bwd_kv<true> : k_bwd_kv<false>;
+    hipLaunchKernelGGL(kern, dim3(Ukv.cap), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout),
                        static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), P, Ukv.list,
-                       P.flags + kSlotKvUnits, H, func, nfunc, alpha, scale);
+                       P.flags + kSlotKvUnits, H, func, nfunc, alpha, scale, pstore);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (pstore) return launch_dq_from_p(k, dq, P, Uq, H, nfunc, pstore, scale, stream);
   if (Uq.cap > 0) {
     ProfScope ps(stream, "k_bwd_q");
     hipLaunchKernelGGL(k_bwd_q, dim3(Uq.cap), dim3(kThreads), 0, stream,

@@ -54,6 +54,8 @@ struct Prep {
   int* tiles64;        // [B+1] prefix over `order` of ceil(L/64)
   int* tiles128;       // [B+1] prefix over `order` of ceil(L/128)
   int4* env;           // [nrb_cap * ni] envelopes {ulo, uhi, ilo, ihi}
+  int64_t* pblk;       // [B+1] prefix of ceil(L/128)*ceil(L/32) (stored-P blocks per
+                       // head of each sequence, original order); null when not planned
   int B;
   int64_t total;
   int nrb_cap;         // capacity of row blocks: ceil(total/64) + B
@@ -72,6 +74,7 @@ struct Plan {
   size_t off_flags, off_so, off_order, off_rb, off_t64, off_t128, off_env;
   size_t off_units_a, off_units_b, off_units_c;  // unit lists (kernel specific)
   size_t off_partial;                             // targets-only partial sums
+  size_t off_pblk = 0;                            // stored-P block prefix (backward)
   int cap_a = 0, cap_b = 0, cap_c = 0;
   int nrb_cap = 0;
   int ni = 0;
@@ -125,10 +128,16 @@ hipError_t launch_generic_bwd(int dtype, int D, const void* q, const void* k, co
 hipError_t launch_mfma_fwd(const void* q, const void* k, const void* v, void* o, const Prep& P,
                            const Units& U, int H, const int32_t* func, int nfunc, float alpha,
                            float inv_max_len, hipStream_t stream);
+// pstore == nullptr: dQ by the query-owner kernel (recomputes S and dS);
+// otherwise the key-owner kernel also stores P (bf16) there and dQ = P K is
+// formed from it by k_bwd_dq.
 hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const void* dout,
                            void* dq, void* dk, void* dv, const Prep& P, const Units& Ukv,
                            const Units& Uq, int H, const int32_t* func, int nfunc, float alpha,
-                           float inv_max_len, hipStream_t stream);
+                           float inv_max_len, uint16_t* pstore, hipStream_t stream);
+hipError_t launch_dq_from_p(const void* k, void* dq, const Prep& P, const Units& Uq, int H,
+                            int nfunc, const uint16_t* pstore, float out_scale,
+                            hipStream_t stream);
 
 // targets-only streaming kernels (any dtype, D); U lists 128-row key tiles
 int targets_chunk_rows();

@@ -137,6 +137,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prep P, const int64_t* __
 
   // 5. row-block offsets (original order) and tile prefixes (dealt order).
   int carry_rb = 0, carry64 = 0, carry128 = 0;
+  int64_t carry_blk = 0;
   for (int base = 0; base < B; base += kPrepThreads) {
     const int b = base + tid;
     int nrb = 0, n64 = 0, n128 = 0;
@@ -160,11 +161,24 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prep P, const int64_t* __
     carry_rb += t_rb;
     carry64 += t64;
     carry128 += t128;
+    if (P.pblk) {
+      // stored-P blocks of one head: (128-key tiles) x (32-row steps)
+      int64_t nblk = 0;
+      if (b < B) {
+        const int L = (int)(P.so[b + 1] - P.so[b]);
+        nblk = (int64_t)cdiv(L, 128) * cdiv(L, 32);
+      }
+      int64_t t_blk;
+      const int64_t i_blk = block_inclusive_scan(nblk, scan64, &t_blk, SumOp());
+      if (b < B) P.pblk[b] = carry_blk + i_blk - nblk;
+      carry_blk += t_blk;
+    }
   }
   if (tid == 0) {
     P.rb_off[B] = carry_rb;
     P.tiles64[B] = carry64;
     P.tiles128[B] = carry128;
+    if (P.pblk) P.pblk[B] = carry_blk;
   }
   if (flags) atomicOr(&sflags, flags);
   __syncthreads();

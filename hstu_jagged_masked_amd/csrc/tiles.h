@@ -187,6 +187,34 @@ __device__ __forceinline__ void dma_barrier() {
   __syncthreads();
 }
 
+// Workgroup barrier ordering LDS accesses only: it waits for this wave's own
+// LDS operations but not for its vector-memory loads, so loads of later
+// tiles stay in flight across it (a plain __syncthreads() may wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// lds_dma16 issued from inline assembly: the same copy, but invisible to the
+// compiler's memory model, which then adds no waits of its own for it (it
+// treats copies into LDS and loads into registers as completing out of order
+// and would wait for every outstanding load before reading any LDS).  The
+// caller orders it explicitly: s_waitcnt vmcnt plus a barrier before the
+// copied data is read, and a barrier before its destination is overwritten.
+// `lds` must be wave-uniform.  M0 is set here; no other code in these kernels
+// keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16_raw(__amdgpu_buffer_rsrc_t r, const void* lds,
+                                              int voffset) {
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0),
+               "v"(voffset), "s"(r)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // A voffset no buffer in this library reaches: its DMA lane writes zeros.
 constexpr int kDmaSkip = 0x7ff00000;
 

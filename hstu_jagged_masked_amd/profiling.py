@@ -26,9 +26,12 @@ import re
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNELS = ("k_fwd_bf16", "k_bwd_kv", "k_bwd_q", "k_targets_fwd", "k_targets_bwd")
-KERNEL_SOURCES = {"k_fwd_bf16": ["fwd.hip"], "k_bwd_kv": ["bwd.hip"], "k_bwd_q": ["bwd.hip"],
-                  "k_targets_fwd": ["targets.hip"], "k_targets_bwd": ["targets.hip"]}
+KERNELS = ("k_fwd_bf16", "k_bwd_kv", "k_bwd_kv_p", "k_bwd_q", "k_bwd_dq", "k_targets_fwd",
+           "k_targets_bwd")
+KERNEL_SOURCES = {"k_fwd_bf16": ["fwd.hip"], "k_bwd_kv": ["bwd.hip"], "k_bwd_kv_p": ["bwd.hip"],
+                  "k_bwd_q": ["bwd.hip"],
+                  "k_bwd_dq": ["dq.hip"], "k_targets_fwd": ["targets.hip"],
+                  "k_targets_bwd": ["targets.hip"]}
 COMMON_SOURCES = ["common.h", "tiles.h"]
 COPY_KERNEL = "__amd_rocclr_copybuffer"  # the HIP runtime's device-to-device copy kernel
 
@@ -42,9 +45,10 @@ def source_digest(kernel: str) -> str:
 
 
 def short_name(name: str) -> str:
-    m = re.search(r"(k_\w+)", name)
+    m = re.search(r"(k_\w+)(<true>)?", name)
     if m and "hstu" in name:
-        return m.group(1)
+        # the key-owner kernel's stored-P instantiation is named as in the library's own timing
+        return m.group(1) + ("_p" if m.group(1) == "k_bwd_kv" and m.group(2) else "")
     return name.split("(")[0][-60:]
 
 

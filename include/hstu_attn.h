@@ -107,6 +107,32 @@ int hstu_attn_bwd(int dtype, const void* q, const void* k, const void* v, const 
                   int64_t max_len, const int32_t* target_rows, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* Stored-P backward (bf16, D = 128, full-length mode): the same outputs as
+ * hstu_attn_bwd (dtype HSTU_BF16, target_rows NULL).  Instead of a query-owner
+ * pass that recomputes <q_i, k_j> and <dO_i, v_j> for dQ, the key-owner pass
+ * also writes, for every 32-row x 128-key block it visits, the bf16 values
+ * max_len * dP_ij that it feeds its own dK product (0 for masked pairs) into
+ * `pstore`, and dQ_i = alpha/max_len * sum_j (max_len dP_ij) k_j is formed
+ * from them.  This trades HBM capacity and bandwidth (about 2 bytes per
+ * (row, column) pair of each sequence's L x L square, per head) for 4*D of
+ * the 14*D executed flops per visible pair.
+ * pstore: device buffer, 256-byte aligned, of at least hstu_attn_pstore_bytes
+ * bytes; scratch (contents not preserved).  The call reads the needed size
+ * back from the device (it synchronizes `stream`, so it cannot be captured in
+ * a HIP graph) and returns HSTU_ERR_WORKSPACE, enqueueing nothing more, when
+ * pstore_bytes is smaller.  dk, dv and dq are deterministic. */
+int hstu_attn_bwd_pstore(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                         void* dk, void* dv, const int64_t* seq_offsets, int64_t B, int64_t total,
+                         int H, int D, const int32_t* func, int nfunc, float alpha,
+                         int64_t max_len, void* workspace, size_t workspace_bytes, void* pstore,
+                         size_t pstore_bytes, void* stream);
+
+/* Bytes of `pstore` that hstu_attn_bwd_pstore needs: the sum over sequences of
+ * ceil(L_b/128) * ceil(L_b/32) * 8192 * H.  seq_offsets is a HOST copy of the
+ * int64 [B+1] offsets (sanitized exactly as the kernels do: clamped into
+ * [0, total], running maximum).  Returns 0 for unsupported sizes. */
+size_t hstu_attn_pstore_bytes(const int64_t* seq_offsets, int64_t B, int64_t total, int H);
+
 /* Visible-column count |V_i| of every query row: counts is int32 [total]
  * (or [B] with target_rows), total_pairs a device int64 receiving their sum.
  * Either output may be NULL.  Integer work: exact. */

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size",
-                            "hstu_attn_fwd", "hstu_attn_bwd", "hstu_attn_visible_counts",
+                            "hstu_attn_fwd", "hstu_attn_bwd", "hstu_attn_bwd_pstore",
+                            "hstu_attn_pstore_bytes", "hstu_attn_visible_counts",
                             "hstu_attn_check_inputs", "hstu_profile_enable",
                             "hstu_profile_read", "hstu_profile_reset"])
 
@@ -125,3 +126,36 @@ def test_profile_toggle_without_device_work(lib):
     assert hj.profile_enable(False) is True
     hj.profile_reset()
     assert hj.profile_read() == {}
+
+
+def _host_offsets(vals):
+    arr = (ctypes.c_int64 * len(vals))(*vals)
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def test_pstore_bytes_closed_form(lib):
+    # lengths 100, 0, 200: ceil(L/128) * ceil(L/32) blocks = 1*4 + 0 + 2*7 = 18 per head
+    keep, off = _host_offsets([0, 100, 100, 300])
+    assert lib.hstu_attn_pstore_bytes(off, 3, 300, 2) == 18 * 2 * 8192
+    # malformed offsets are sanitized as the kernels do: clamp, running max
+    keep, off = _host_offsets([0, 50, 30, 100])
+    assert lib.hstu_attn_pstore_bytes(off, 3, 100, 1) == (2 + 0 + 2) * 8192
+    keep, off = _host_offsets([0, 4096])
+    assert lib.hstu_attn_pstore_bytes(off, 1, 4096, 4) == 32 * 128 * 4 * 8192
+    assert lib.hstu_attn_pstore_bytes(None, 1, 10, 1) == 0
+    keep, off = _host_offsets([0, 10])
+    assert lib.hstu_attn_pstore_bytes(off, 1, 10, 0) == 0
+
+
+def test_bwd_pstore_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    f = P(FAKE)
+
+    def call(D=128, pstore=f, ws_bytes=1 << 20):
+        return lib.hstu_attn_bwd_pstore(f, f, f, f, f, f, f, f, 2, 10, 2, D, f, 5, 0.1, 8, f,
+                                        ws_bytes, pstore, 1 << 20, None)
+
+    assert call(D=64) == -2 and "D = 128" in lib.hstu_last_error().decode()
+    assert call(pstore=None) == -1 and "pstore is NULL" in lib.hstu_last_error().decode()
+    assert call(pstore=P(FAKE + 16)) == -1 and "256-byte" in lib.hstu_last_error().decode()
+    assert call(ws_bytes=16) == -3

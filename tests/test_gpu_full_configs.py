@@ -63,23 +63,27 @@ def to64(x):
     return x.float().cpu().numpy().astype(np.float64)
 
 
-def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False):
+def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False, pstore=False):
     """fwd+bwd on the whole workload; oracle on the sequences `seqs`.  With
     `repeat`, a second fwd+bwd must reproduce every output bit for bit (each
     output element is written by one workgroup in a fixed order, so any
     difference is a race)."""
     t, off = device_inputs(cfg)
     func = torch.from_numpy(func_np).to(DEV)
+    ps = None
+    if pstore:
+        ps = torch.empty(hj.pstore_bytes(t["off"], cfg["H"]), dtype=torch.uint8, device=DEV)
     o = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], func, cfg["alpha"], cfg["max_len"])
     dq, dk, dv = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
-                             cfg["max_len"])
+                             cfg["max_len"], pstore=ps)
     if repeat:
         o2 = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], func, cfg["alpha"], cfg["max_len"])
         g2 = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
-                         cfg["max_len"])
+                         cfg["max_len"], pstore=ps)
         for nm, a, b in zip(("o", "dq", "dk", "dv"), (o, dq, dk, dv), (o2,) + tuple(g2)):
             assert torch.equal(a, b), f"{cfg['name']}.{nm}: second run differs"
         del o2, g2
+    del ps
     torch.cuda.synchronize()
     rows, sub_off = oracle.subset(off, seqs)
     rows_t = torch.from_numpy(rows).to(DEV)
@@ -136,6 +140,14 @@ def test_hstu_layer_shapes_sampled(hj, name):
     counts, tot = hj.visible_counts(off_t, torch.from_numpy(f).to(DEV), int(ls.sum()))
     assert np.array_equal(counts.cpu().numpy(), wl.local_rows(ls) + 1), "causal counts"
     assert int(tot.item()) == int(np.sum(ls * (ls + 1) // 2))
+
+
+def test_hstu_2663_pstore_sampled(hj):
+    """The stored-P backward at the benchmark shape (a 58 GB P buffer)."""
+    cfg = wl.workload("hstu_2663")
+    ls = cfg["lengths"]
+    run_full(hj, cfg, cfg["func"](ls, 5), sample_seqs(ls), nfunc_label=".pstore", repeat=True,
+             pstore=True)
 
 
 def test_three_interval_sampled(hj):

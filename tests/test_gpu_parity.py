@@ -72,7 +72,12 @@ def assert_parity(name, got_t, want, dtype):
     return err, rel
 
 
-def run_case(hj, lengths, H, D, dtype, func, alpha, max_len, seed=7, targets=None, bwd=True):
+def pstore_for(hj, off_t, H):
+    return torch.empty(max(hj.pstore_bytes(off_t, H), 256), dtype=torch.uint8, device=DEV)
+
+
+def run_case(hj, lengths, H, D, dtype, func, alpha, max_len, seed=7, targets=None, bwd=True,
+             pstore=False):
     lengths = np.asarray(lengths, dtype=np.int64)
     off = wl.offsets_from_lengths(lengths)
     inp = make_inputs(lengths, H, D, dtype, seed, targets)
@@ -85,7 +90,8 @@ def run_case(hj, lengths, H, D, dtype, func, alpha, max_len, seed=7, targets=Non
     want_o = oracle.fwd(qn, kn, vn, off, func, alpha, max_len, targets)
     res = {"o": assert_parity("o", o, want_o, dtype)}
     if bwd:
-        dq, dk, dv = hj.attn_bwd(q, k, v, do, off_t, func_t, alpha, max_len, tr_t)
+        ps = pstore_for(hj, off_t, q.shape[1]) if pstore else None
+        dq, dk, dv = hj.attn_bwd(q, k, v, do, off_t, func_t, alpha, max_len, tr_t, pstore=ps)
         torch.cuda.synchronize()
         wq, wk, wv = oracle.bwd(qn, kn, vn, don, off, func, alpha, max_len, targets)
         res["dq"] = assert_parity("dq", dq, wq, dtype)
@@ -259,3 +265,57 @@ def test_malformed_offsets_stay_in_bounds(hj):
     g = hj.attn_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], bad, ft, 0.1, 100)
     torch.cuda.synchronize()
     assert o.shape == inp["q"][0].shape and g[0].shape == o.shape
+
+
+# --- the stored-P backward (bf16, D = 128) ------------------------------------
+
+PSTORE_CASES = {
+    "causal_ragged": (RAGGED, lambda ls: wl.func_causal(ls, 5), 1 / np.sqrt(128), 300),
+    "sla": ([600, 333, 1000], lambda ls: wl.func_sla(ls, 256, 32, 5), 1 / np.sqrt(128), 1000),
+    "three_interval": ([300, 520, 270, 100], lambda ls: wl.func_three_interval(ls, 32, 8, 5),
+                       1 / np.sqrt(128), 520),
+    "random_nfunc9": ([5, 0, 77, 200, 64, 65], lambda ls: wl.func_random(ls, 9, 109, spread=20),
+                      0.1, 200),
+    "long_windows": ([4700, 130, 4160], lambda ls: wl.func_sla(ls, 1200, 32, 5),
+                     1 / np.sqrt(128), 4700),
+    "single_rows": ([1, 0, 3, 0], lambda ls: wl.func_causal(ls, 5), 0.5, 3),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PSTORE_CASES))
+def test_bf16_pstore_backward(hj, name):
+    lengths, fn, alpha, max_len = PSTORE_CASES[name]
+    ls = np.array(lengths)
+    H = 1 if name == "long_windows" else 2
+    run_case(hj, ls, H, 128, "bf16", fn(ls), alpha, max_len, seed=31, pstore=True)
+
+
+def test_bf16_pstore_dk_dv_bitwise_equal_recompute_path(hj):
+    """The stored-P key-owner pass computes dK and dV exactly as the default
+    one (it only adds the stores); dQ comes from another kernel."""
+    ls = np.array([700, 128, 900, 1, 0])
+    off = wl.offsets_from_lengths(ls)
+    off_t = torch.from_numpy(off).to(DEV)
+    inp = make_inputs(ls, 4, 128, "bf16", 33)
+    f = torch.from_numpy(wl.func_sla(ls, 256, 32, 5)).to(DEV)
+    args = (inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], off_t, f, 0.09, 900)
+    dq0, dk0, dv0 = hj.attn_bwd(*args)
+    dq1, dk1, dv1 = hj.attn_bwd(*args, pstore=pstore_for(hj, off_t, 4))
+    dq2, dk2, dv2 = hj.attn_bwd(*args, pstore=pstore_for(hj, off_t, 4))
+    assert torch.equal(dk0, dk1) and torch.equal(dv0, dv1)
+    assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    err = (dq0.float() - dq1.float()).abs().max().item()
+    assert err <= 2e-2 * dq0.float().abs().max().item()
+
+
+def test_bf16_pstore_buffer_too_small(hj):
+    ls = np.array([300, 200])
+    off_t = torch.from_numpy(wl.offsets_from_lengths(ls)).to(DEV)
+    inp = make_inputs(ls, 2, 128, "bf16", 34)
+    f = torch.from_numpy(wl.func_causal(ls, 5)).to(DEV)
+    need = hj.pstore_bytes(off_t, 2)
+    assert need == (3 * 10 + 2 * 7) * 2 * 8192
+    small = torch.empty(need - 8192, dtype=torch.uint8, device=DEV)
+    with pytest.raises(hj.HstuError, match="stored-P buffer"):
+        hj.attn_bwd(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], off_t, f, 0.1, 300,
+                    pstore=small)
