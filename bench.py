@@ -111,6 +111,28 @@ def timed(hj, torch, t, cfg, steps, targets=False, pstore=None):
     return e0.elapsed_time(e1) / steps, wall, prof
 
 
+def split_ms(hj, torch, t, cfg, steps, pstore):
+    """Forward alone and backward alone, `steps` calls each (after the timed
+    region; HIP events on the current stream)."""
+    out = {}
+    for name in ("fwd", "bwd"):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            if name == "fwd":
+                hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], t["func"], cfg["alpha"],
+                            cfg["max_len"])
+            else:
+                hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], t["func"], cfg["alpha"],
+                            cfg["max_len"], pstore=pstore)
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / steps, 4)
+    return out
+
+
 def cpu_baseline(cfg, t, off, nseq):
     """The fp64 oracle on the first `nseq` sequences (fwd + bwd), host cores."""
     import oracle
@@ -194,6 +216,7 @@ def main():
     log(f"[bench] warmup done ({args.warmup} steps)")
     ms, wall, prof = timed(hj, torch, t, cfg, args.steps, pstore=pstore)
     log(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step")
+    split = split_ms(hj, torch, t, cfg, args.steps, pstore)
     flops_eff = 14.0 * D * H * pairs
     value = flops_eff / (ms * 1e-3) / 1e12
 
@@ -233,6 +256,20 @@ def main():
                            for k, (c, m) in sorted(t_prof.items())}}
     del tt
 
+    # cost of padded empty intervals: the SLA 2k workload (B=16, S=2048, H=8)
+    # with its two intervals encoded as nfunc=3 and padded to nfunc=5
+    c3 = wl.workload("sla_2k")
+    t3, _ = make_inputs(c3, device)
+    pad = {"workload": "sla_2k"}
+    for nf in (3, 5):
+        t3["func"] = torch.from_numpy(c3["func"](c3["lengths"], nf)).to(device)
+        run_steps(hj, t3, c3, 3)
+        m3, _, _ = timed(hj, torch, t3, c3, 20)
+        pad[f"ms_nfunc{nf}"] = round(m3, 4)
+    pad["delta_pct"] = round(100.0 * (pad["ms_nfunc5"] / pad["ms_nfunc3"] - 1.0), 2)
+    del t3
+    log(f"[bench] sla_2k nfunc 3 vs 5: {pad}")
+
     cpu = None
     if args.cpu_seqs > 0:
         log(f"[bench] cpu oracle baseline on {args.cpu_seqs} sequences ...")
@@ -259,9 +296,13 @@ def main():
                    "dq_path": "stored_p" if use_p else "recompute",
                    "pstore_gb": round(p_bytes / 1e9, 2) if use_p else 0.0},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        # the same step counted at 12*D per pair (no recomputed products)
+        "value_12d": round(12.0 * D * H * pairs / (ms * 1e-3) / 1e12, 2),
+        "split_ms": split,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "targets_only": targets,
+        "nfunc_pad_cost": pad,
         "kernels": kernels,
         "wall_s_timed": round(wall, 3),
     }

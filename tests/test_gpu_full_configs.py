@@ -165,6 +165,21 @@ def test_three_interval_sampled(hj):
     assert np.array_equal(counts[rows], want)
 
 
+@pytest.mark.parametrize("pstore", [False, True])
+def test_onerank_sampled(hj, pstore):
+    cfg = wl.workload("onerank")
+    ls = cfg["lengths"]
+    f = cfg["func"](ls, 5)
+    seqs = sample_seqs(ls)
+    run_full(hj, cfg, f, seqs, nfunc_label=".pstore" if pstore else "", pstore=pstore)
+    off = wl.offsets_from_lengths(ls)
+    off_t = torch.from_numpy(off).to(DEV)
+    counts, tot = hj.visible_counts(off_t, torch.from_numpy(f).to(DEV), int(off[-1]))
+    H = ls - 240
+    want = sum(int(h) * (int(h) + 1) // 2 + 60 * (int(h) + 1) + 180 * (int(h) + 2) for h in H)
+    assert int(tot.item()) == want
+
+
 def test_hstu_2663_targets_only_sampled(hj):
     """Targets-only at the production shape: candidates of 64 sampled
     sequences checked (o, dq for the candidates; dk, dv for all their rows)."""

@@ -183,6 +183,15 @@ def test_bf16_three_interval(hj):
              520, seed=14)
 
 
+def test_bf16_onerank(hj):
+    """OneRank task-private masks: history, then candidate + 3 task tokens per
+    group; each task token sees the history, its candidate and itself."""
+    n_cand = np.array([8, 4, 60, 1, 30])
+    ls = wl.onerank_lengths([100, 2, 1968, 0, 300], n_cand, 3)
+    run_case(hj, ls, 2, 128, "bf16", wl.func_onerank(ls, n_cand, 3, 5), 1 / np.sqrt(128),
+             int(ls.max()), seed=22)
+
+
 @pytest.mark.parametrize("nfunc", [1, 3, 5, 9])
 def test_bf16_random_func(hj, nfunc):
     ls = np.array([5, 0, 77, 200, 64, 65])
@@ -279,6 +288,8 @@ PSTORE_CASES = {
     "long_windows": ([4700, 130, 4160], lambda ls: wl.func_sla(ls, 1200, 32, 5),
                      1 / np.sqrt(128), 4700),
     "single_rows": ([1, 0, 3, 0], lambda ls: wl.func_causal(ls, 5), 0.5, 3),
+    "onerank": (list(wl.onerank_lengths([100, 2, 1968, 300], [8, 4, 60, 30], 3)),
+                lambda ls: wl.func_onerank(ls, [8, 4, 60, 30], 3, 5), 1 / np.sqrt(128), 2208),
 }
 
 

@@ -159,6 +159,49 @@ def func_three_interval(lengths, n_blocks: int = 32, block: int = 8, nfunc: int 
     return _pack(list(f), nfunc)
 
 
+def onerank_lengths(history, n_candidates, k_tasks: int = 3) -> np.ndarray:
+    """Sequence lengths of the OneRank layout: history plus, per candidate, the
+    candidate token followed by its K task tokens (groups of K + 1)."""
+    history = np.asarray(history, dtype=np.int64)
+    n_candidates = np.asarray(n_candidates, dtype=np.int64)
+    return history + n_candidates * (k_tasks + 1)
+
+
+def func_onerank(lengths, n_candidates, k_tasks: int = 3, nfunc: int = 5) -> np.ndarray:
+    """OneRank task-private masks (TorchEasyRec PR #670 follow-up commit, the
+    build_onerank_func_tensor note).
+
+    Sequence b holds a history of H_b = L_b - n_b (K + 1) rows, then n_b groups
+    of K + 1 rows: candidate e_i followed by task tokens t_1..t_K.  Task token
+    t_k of group i sees [0, H_b), e_i and itself -- three intervals, because the
+    other task tokens of the group lie between e_i and t_k.  Readings (the note
+    states only the task tokens' set): history rows are causal, [0, r+1); a
+    candidate sees the history and itself.  K = 3 matches the note's length
+    examples (148 -> 132, 26 -> 18, 2328 -> 2208 when each candidate stops
+    being replicated once per task token).
+    """
+    if nfunc < 5:
+        raise ValueError("task tokens need three intervals (nfunc >= 5)")
+    lengths = np.asarray(lengths, dtype=np.int64)
+    n_candidates = np.broadcast_to(np.asarray(n_candidates, dtype=np.int64), lengths.shape)
+    hist = lengths - n_candidates * (k_tasks + 1)
+    if np.any(hist < 0):
+        raise ValueError("a sequence is shorter than its candidate groups")
+    i = local_rows(lengths)
+    H = np.repeat(hist, lengths)
+    in_hist = i < H
+    g = np.where(in_hist, 0, (i - H) // (k_tasks + 1))        # group of a candidate row
+    pos = np.where(in_hist, 0, (i - H) % (k_tasks + 1))       # 0 = candidate, k = task k
+    cand = H + g * (k_tasks + 1)                              # the group's candidate row
+    f0 = np.where(in_hist, i + 1, H)
+    f1 = np.where(in_hist, f0, cand)
+    f2 = np.where(in_hist, f0, cand + 1)
+    is_task = (~in_hist) & (pos > 0)
+    f3 = np.where(is_task, i, f2)
+    f4 = np.where(is_task, i + 1, f2)
+    return _pack([f0, f1, f2, f3, f4], nfunc)
+
+
 def func_random(lengths, nfunc: int, seed: int, spread: int = 4) -> np.ndarray:
     """Arbitrary int32 bounds, including negative, past-the-end, reversed and
     overlapping pairs, for decode tests on small inputs."""
@@ -235,6 +278,8 @@ def workload(name: str):
       hstu_ragged    B=1024 L~U{1332..3994} (seed 41), otherwise as hstu_2663
       hstu_4086      B=1024 L=4086, otherwise as hstu_2663
       three_interval B=256 L~U{512..4096} (seed 5) H=4 D=128 bf16, 3 intervals
+      onerank        B=256, 60 candidates x (1 + 3 task tokens) after a history
+                     H~U{272..3856} (seed 6), H=4 D=128 bf16, the OneRank layout
     """
     if name == "tiny_fp32":
         lengths = np.array([37, 64], dtype=np.int64)
@@ -266,8 +311,15 @@ def workload(name: str):
         return dict(name=name, lengths=lengths, H=4, D=128, dtype="bf16",
                     func=lambda ls, nf=5: func_three_interval(ls, 32, 8, nf), nfunc=5,
                     alpha=1.0 / np.sqrt(128.0), max_len=int(lengths.max()), seed=5)
+    if name == "onerank":
+        hist = lengths_ragged(256, 272, 3856, 6)
+        n_cand = np.full(256, 60, dtype=np.int64)
+        lengths = onerank_lengths(hist, n_cand, 3)
+        return dict(name=name, lengths=lengths, H=4, D=128, dtype="bf16",
+                    func=lambda ls, nf=5: func_onerank(ls, n_cand, 3, nf), nfunc=5,
+                    alpha=1.0 / np.sqrt(128.0), max_len=int(lengths.max()), seed=6)
     raise KeyError(name)
 
 
 WORKLOADS = ("tiny_fp32", "sla_1k", "sla_2k", "hstu_2663", "hstu_ragged", "hstu_4086",
-             "three_interval")
+             "three_interval", "onerank")
