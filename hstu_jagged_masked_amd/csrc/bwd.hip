@@ -13,9 +13,10 @@
 // every gradient is bitwise repeatable:
 //   k_bwd_kv  one workgroup per (sequence, head, 128 key rows); wave w owns keys
 //             [32w, 32w+32) and keeps their K and V rows in registers; wave 0
-//             lists, with a ballot, the 32-row query steps whose row blocks'
-//             envelopes reach these keys (partly seen blocks and wholly seen
-//             blocks in separate lists); for each step:
+//             lists, with a ballot, the 64-row row blocks whose envelopes
+//             reach these keys (partly seen blocks and wholly seen blocks in
+//             separate lists); each block is one step (one LDS stage, one
+//             barrier), computed as two halves of 32 query rows:
 //               S = Q K^T, dS = dO V^T          (A from LDS, B = K, V registers)
 //               y, p in registers (mask via per-row bitmasks in LDS)
 //               dV^T += dO^T Y,  dK^T += Q^T P  (A = transpose reads of the
@@ -45,9 +46,10 @@ using S1 = std::integral_constant<int, 1>;
 // k_bwd_kv
 constexpr int kKvBN = 128;                    // key rows per workgroup
 constexpr int kKvBM = 32;                     // query rows per step (half a row block)
-constexpr int kQStage = kKvBM * kD;           // bf16 elements per swizzled stage (8 KiB)
-constexpr int kQInstr = kQStage / 512;        // 8 wave DMA instructions per tile
-constexpr int kStepWin = 2 * kListWin;        // steps per list window (two per row block)
+constexpr int kStepRows = 2 * kKvBM;          // query rows per step (one row block)
+constexpr int kQStage = kStepRows * kD;       // bf16 elements per swizzled stage (16 KiB)
+constexpr int kQInstr = kQStage / 512;        // 16 wave DMA instructions per tile
+constexpr int kStepWin = kListWin;            // steps per list window (one per row block)
 
 // k_bwd_q
 constexpr int kQBM = 128;                     // query rows per workgroup
@@ -60,9 +62,9 @@ __device__ __forceinline__ bf16x8 concat4(bf16x4 a, bf16x4 b) {
 }
 
 // Wave-level: for the row blocks [w0, min(w0 + 64, nrb)) of a sequence of
-// length L, lists the 32-row steps (their first local row) of the blocks that
-// reach key columns [c0, c1): partly seen blocks into part, wholly seen ones
-// into full; returns the counts in every lane.
+// length L, lists the blocks (their first local row) that reach key columns
+// [c0, c1): partly seen blocks into part, wholly seen ones into full; returns
+// the counts in every lane.
 __device__ __forceinline__ void step_window(const int4* env, int ni, int L, int nrb, int w0,
                                             int c0, int c1, int* part, int* full_list,
                                             int& n_part, int& n_full) {
@@ -72,22 +74,12 @@ __device__ __forceinline__ void step_window(const int4* env, int ni, int L, int 
   if (rb < nrb) block_vs_cols(env + (int64_t)rb * ni, ni, c0, c1, live, full);
   full = full && live;
   const bool partial = live && !full;
-  const bool second = rb * kRB + kKvBM < L;  // the block has a second 32-row step
   const uint64_t below = (1ull << lane) - 1ull;
-  const uint64_t mp = __ballot(partial), mp2 = __ballot(partial && second);
-  const uint64_t mf = __ballot(full), mf2 = __ballot(full && second);
-  if (partial) {
-    const int pos = __popcll(mp & below) + __popcll(mp2 & below);
-    part[pos] = rb * kRB;
-    if (second) part[pos + 1] = rb * kRB + kKvBM;
-  }
-  if (full) {
-    const int pos = __popcll(mf & below) + __popcll(mf2 & below);
-    full_list[pos] = rb * kRB;
-    if (second) full_list[pos + 1] = rb * kRB + kKvBM;
-  }
-  n_part = __popcll(mp) + __popcll(mp2);
-  n_full = __popcll(mf) + __popcll(mf2);
+  const uint64_t mp = __ballot(partial), mf = __ballot(full);
+  if (partial) part[__popcll(mp & below)] = rb * kRB;
+  if (full) full_list[__popcll(mf & below)] = rb * kRB;
+  n_part = __popcll(mp);
+  n_full = __popcll(mf);
 }
 
 // kStoreP: also store each step's P (bf16, as rounded for the dK product) for
@@ -113,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   // filling one stage does not alias the reads of the other
   __shared__ __attribute__((aligned(256))) uint16_t sQ0[kQStage], sQ1[kQStage];
   __shared__ __attribute__((aligned(256))) uint16_t sG0[kQStage], sG1[kQStage];  // dO
-  __shared__ __attribute__((aligned(16))) uint32_t sMask[4][kKvBM];
+  __shared__ __attribute__((aligned(16))) uint32_t sMask[4][kStepRows];
   __shared__ int sPart[kStepWin], sFull[kStepWin];
   __shared__ int sCount[2];
   // P staging: per wave [32 keys][32 row positions], 64-byte rows
@@ -184,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
       p_pending = -1;
     }
   };
-  // DMA of one 32-row step: wave w issues instructions I = w + 4i of each
+  // DMA of one 64-row step: wave w issues instructions I = w + 4i of each
   // tensor; lane l of instruction I fills LDS slot 64*I + l
   constexpr int kDmaPerWave = kQInstr / 4;
   int doff[kDmaPerWave];
@@ -192,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   for (int i = 0; i < kDmaPerWave; ++i) doff[i] = swz_dma_offset((wave + 4 * i) * 64 + lane, rs2);
   auto dma_step = [&](int q0, auto stage) {
     constexpr int st = decltype(stage)::value;
-    const int rows = min(kKvBM, L - q0);
+    const int rows = min(kStepRows, L - q0);
     const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qh + (int64_t)q0 * rs, rows, rs2, kD * 2);
     const __amdgpu_buffer_rsrc_t rg = rows_rsrc(gh + (int64_t)q0 * rs, rows, rs2, kD * 2);
 #pragma unroll
@@ -216,16 +208,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
                     ((((grp & 1) * 2 + ((gl & 3) >> 1)) ^ swz(trow)) << 4);
   const int32_t* fseq = func + s;
 
-  // one 32-row step from LDS stage `stage`; `next` (>= 0) is the next step's
-  // first row, whose DMA is issued after this step's func loads
+  // one 64-row step (two halves of 32 rows) from LDS stage `stage`; `next`
+  // (>= 0) is the next step's first row, whose DMA is issued after this
+  // step's func loads
   auto step = [&](int q0, int next, auto masked, auto stage) {
     constexpr bool kMasked = decltype(masked)::value;
     constexpr int st = decltype(stage)::value;
-    const uint16_t* sQ = st ? sQ1 : sQ0;
-    const uint16_t* sG = st ? sG1 : sG0;
-    const int rd_b = opaque(rd_b0), tr_b = opaque(tr_b0);
-    int lo[kMaxNI], hi[kMaxNI];
-    if constexpr (kMasked) row_intervals_rsrc(fseq, P.total, q0 + n, ni, L, lo, hi);
+    const int nh = q0 + kKvBM < L ? 2 : 1;  // halves of 32 rows in this step
+    if constexpr (kMasked) {
+      // rows q0 + 32 hf + n: visibility of this wave's 32 key columns
+      // (wave-private LDS), before the next step's copies so the func loads
+      // do not wait behind them
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        int lo[kMaxNI], hi[kMaxNI];
+        row_intervals_rsrc(fseq, P.total, q0 + hf * kKvBM + n, ni, L, lo, hi);
+        if (g == 0) sMask[wave][hf * kKvBM + n] = col_mask32(lo, hi, ni, c0 + wave * 32);
+      }
+    }
     if (next >= 0) {
       if constexpr (st == 0) {
         dma_step(next, S1{});
@@ -233,64 +233,66 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
         dma_step(next, S0{});
       }
     }
-    if constexpr (kMasked) {
-      // row q0 + n: visibility of this wave's 32 key columns (wave-private
-      // LDS), built before the MFMAs so the intervals are dead during them
-      if (g == 0) sMask[wave][n] = col_mask32(lo, hi, ni, c0 + wave * 32);
-    }
-    // the previous step's P (after the mask, whose func loads must not wait
-    // behind stores)
-    p_flush();
-    f32x16 sacc = f32x16{}, dsacc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) {
-      const int off = rd_b ^ (32 * ks);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row16(sQ, off), kf[ks], sacc, 0, 0, 0);
-      dsacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row16(sG, off), vf[ks], dsacc, 0, 0, 0);
-    }
-    // element r: query row (r/4)*8 + g*4 + r%4 of the step, key column `col`
-    bf16x8 yb[2], pb[2];
+    for (int hf = 0; hf < 2; ++hf) {
+      if (hf >= nh) break;
+      const uint16_t* sQ = (st ? sQ1 : sQ0) + hf * kKvBM * kD;
+      const uint16_t* sG = (st ? sG1 : sG0) + hf * kKvBM * kD;
+      const int rd_b = opaque(rd_b0), tr_b = opaque(tr_b0);
+      // the previous half's P
+      p_flush();
+      f32x16 sacc = f32x16{}, dsacc = f32x16{};
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      uint4 m4 = make_uint4(0, 0, 0, 0);
-      if constexpr (kMasked) m4 = *reinterpret_cast<const uint4*>(&sMask[wave][jj * 8 + g * 4]);
-      const uint32_t mrow[4] = {m4.x, m4.y, m4.z, m4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = jj * 4 + i;
-        const float x = sacc[r];
-        const float sg = logistic_scaled(x, c_exp);
-        float y = x * sg;
-        // silu'(alpha x) = sg + alpha * x sg (1 - sg) = sg + alpha * (y - y sg)
-        float p = dsacc[r] * fmaf(alpha, fmaf(-y, sg, y), sg);
-        if constexpr (kMasked) {
-          if (!((mrow[i] >> n) & 1u)) {
-            y = 0.f;
-            p = 0.f;
-          }
-        }
-        yb[r >> 3][r & 7] = (__bf16)y;
-        pb[r >> 3][r & 7] = (__bf16)p;
+      for (int ks = 0; ks < kD / 16; ++ks) {
+        const int off = rd_b ^ (32 * ks);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row16(sQ, off), kf[ks], sacc, 0, 0, 0);
+        dsacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row16(sG, off), vf[ks], dsacc, 0, 0, 0);
       }
-    }
-    if constexpr (kStoreP) {
-      // stage [key n][row position hh*16 + g*8 + e]; stored by the next step
-      *reinterpret_cast<bf16x8*>(p_stage + n * 32 + g * 8) = pb[0];
-      *reinterpret_cast<bf16x8*>(p_stage + n * 32 + 16 + g * 8) = pb[1];
-      p_pending = q0;
-    }
-    // dV^T += dO^T Y and dK^T += Q^T P: A operands by transpose reads, query
-    // rows 16hh + 4g + {0..3} and 16hh + 8 + 4g + {0..3}
+      // element r: query row (r/4)*8 + g*4 + r%4 of the half, key column `col`
+      bf16x8 yb[2], pb[2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+      for (int jj = 0; jj < 4; ++jj) {
+        uint4 m4 = make_uint4(0, 0, 0, 0);
+        if constexpr (kMasked)
+          m4 = *reinterpret_cast<const uint4*>(&sMask[wave][hf * kKvBM + jj * 8 + g * 4]);
+        const uint32_t mrow[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
-      for (int mb = 0; mb < kD / 32; ++mb) {
-        const int o0 = (tr_b ^ (64 * mb)) + 16 * hh * 256;
-        const int o1 = (tr_b ^ (64 * mb) ^ 32) + (16 * hh + 8) * 256;
-        const bf16x8 ag = concat4(lds_tr8(sG, o0), lds_tr8(sG, o1));
-        dvacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, yb[hh], dvacc[mb], 0, 0, 0);
-        const bf16x8 aq = concat4(lds_tr8(sQ, o0), lds_tr8(sQ, o1));
-        dkacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, pb[hh], dkacc[mb], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const int r = jj * 4 + i;
+          const float x = sacc[r];
+          const float sg = logistic_scaled(x, c_exp);
+          float y = x * sg;
+          // silu'(alpha x) = sg + alpha * x sg (1 - sg) = sg + alpha * (y - y sg)
+          float p = dsacc[r] * fmaf(alpha, fmaf(-y, sg, y), sg);
+          if constexpr (kMasked) {
+            if (!((mrow[i] >> n) & 1u)) {
+              y = 0.f;
+              p = 0.f;
+            }
+          }
+          yb[r >> 3][r & 7] = (__bf16)y;
+          pb[r >> 3][r & 7] = (__bf16)p;
+        }
+      }
+      if constexpr (kStoreP) {
+        // stage [key n][row position hh*16 + g*8 + e]; stored by the next half
+        *reinterpret_cast<bf16x8*>(p_stage + n * 32 + g * 8) = pb[0];
+        *reinterpret_cast<bf16x8*>(p_stage + n * 32 + 16 + g * 8) = pb[1];
+        p_pending = q0 + hf * kKvBM;
+      }
+      // dV^T += dO^T Y and dK^T += Q^T P: A operands by transpose reads, query
+      // rows 16hh + 4g + {0..3} and 16hh + 8 + 4g + {0..3}
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int mb = 0; mb < kD / 32; ++mb) {
+          const int o0 = (tr_b ^ (64 * mb)) + 16 * hh * 256;
+          const int o1 = (tr_b ^ (64 * mb) ^ 32) + (16 * hh + 8) * 256;
+          const bf16x8 ag = concat4(lds_tr8(sG, o0), lds_tr8(sG, o1));
+          dvacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, yb[hh], dvacc[mb], 0, 0, 0);
+          const bf16x8 aq = concat4(lds_tr8(sQ, o0), lds_tr8(sQ, o1));
+          dkacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, pb[hh], dkacc[mb], 0, 0, 0);
+        }
       }
     }
   };
