@@ -70,9 +70,9 @@ bool plan_workspace(Plan& p, int is_bwd, int dtype, int64_t B, int64_t total, in
   p.cap_a = round8(cap128);
   p.cap_b = is_bwd ? round8(cap128) : 0;
   p.cap_c = is_bwd ? round8(cap128) : 0;
-  p.off_units_a = take((size_t)p.cap_a * sizeof(int4));
-  p.off_units_b = take((size_t)p.cap_b * sizeof(int4));
-  p.off_units_c = take((size_t)p.cap_c * sizeof(int4));
+  p.off_units_a = take((size_t)p.cap_a * 2 * sizeof(int4));
+  p.off_units_b = take((size_t)p.cap_b * 2 * sizeof(int4));
+  p.off_units_c = take((size_t)p.cap_c * 2 * sizeof(int4));
   p.partial_bytes = 0;
   if (targets_only) {
     const int64_t nchunk = cdiv64(total, targets_chunk_rows()) + B;

@@ -98,9 +98,9 @@ template <bool kStoreP>
 __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, Prep P, const int4* __restrict__ units,
-    const int* __restrict__ unit_count, int H, const int32_t* __restrict__ func, int nfunc,
-    float alpha, float out_scale, uint16_t* __restrict__ pstore) {
+    uint16_t* __restrict__ dv, Prep P, const int4* __restrict__ units, int H,
+    const int32_t* __restrict__ func, int nfunc, float alpha, float out_scale,
+    uint16_t* __restrict__ pstore) {
   // two LDS stages as separate objects, so the compiler sees that the DMA
   // filling one stage does not alias the reads of the other
   __shared__ __attribute__((aligned(256))) uint16_t sQ0[kQStage], sQ1[kQStage];
@@ -111,12 +111,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   // P staging: per wave [32 keys][32 row positions], 64-byte rows
   __shared__ __attribute__((aligned(16))) uint16_t sPst[kStoreP ? 4 * 1024 : 8];
 
-  const int slot = xcd_slot(blockIdx.x, *unit_count);
-  if (slot < 0) return;
-  const int4 u = units[slot];
-  const int b = uniform(u.x), kt = uniform(u.y), h = uniform(u.z);
-  const int64_t s = uniform(P.so[b]);
-  const int L = uniform((int)(P.so[b + 1] - s));
+  UnitRec u;
+  if (!unit_of_block(units, u)) return;
+  const int kt = u.tile, h = u.h, L = u.L;
+  const int64_t s = u.s;
   const int c0 = kt * kKvBN;
   const int c1 = min(c0 + kKvBN, L);
   const int tid = threadIdx.x;
@@ -154,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   int p_pending = -1;  // first row of the step whose P sits in sPst, or -1
   if constexpr (kStoreP) {
     const int64_t nkt = (L + kKvBN - 1) / kKvBN, nsteps = (L + kKvBM - 1) / kKvBM;
-    p_blk0 = uniform(P.pblk[b] * H + h * nkt * nsteps + kt * nsteps);
+    p_blk0 = u.pblk * H + h * nkt * nsteps + kt * nsteps;
   }
   uint16_t* const p_stage = sPst + (kStoreP ? wave * 1024 : 0);
   // transpose reads of the staging rows: lane j of 16-lane group G reads key
@@ -311,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   };
 
   const int nrb = (L + kRB - 1) / kRB;
-  const int4* env = P.env + (int64_t)P.rb_off[b] * ni;
+  const int4* env = P.env + (int64_t)u.rb * ni;
   for (int w0 = 0; w0 < nrb; w0 += kListWin) {
     if (wave == 0) {
       int np, nf;
@@ -354,20 +352,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
 __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq,
-    Prep P, const int4* __restrict__ units, const int* __restrict__ unit_count, int H,
-    const int32_t* __restrict__ func, int nfunc, float alpha, float out_scale) {
+    Prep P, const int4* __restrict__ units, int H, const int32_t* __restrict__ func, int nfunc,
+    float alpha, float out_scale) {
   __shared__ __attribute__((aligned(256))) uint16_t sK0[kKStage], sK1[kKStage];
   __shared__ __attribute__((aligned(256))) uint16_t sV0[kKStage], sV1[kKStage];
   __shared__ int sPart[kListWin], sFull[kListWin];
   __shared__ int sCount[2];
   __shared__ Envelope sEnv;
 
-  const int slot = xcd_slot(blockIdx.x, *unit_count);
-  if (slot < 0) return;
-  const int4 u = units[slot];
-  const int b = uniform(u.x), qt = uniform(u.y), h = uniform(u.z);
-  const int64_t s = uniform(P.so[b]);
-  const int L = uniform((int)(P.so[b + 1] - s));
+  UnitRec u;
+  if (!unit_of_block(units, u)) return;
+  const int qt = u.tile, h = u.h, L = u.L;
+  const int64_t s = u.s;
   const int r0 = qt * kQBM;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -396,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
     hi[j] = 0;
     if (j < ni && row_ok) row_interval(func, P.total, s + row, j, L, lo[j], hi[j]);
   }
-  if (tid == 0) rows_envelope(P, b, r0, kQBM, L, ni, sEnv);
+  if (tid == 0) rows_envelope(P, u.rb, r0, kQBM, L, ni, sEnv);
   __syncthreads();
   int t_begin, t_end;
   envelope_tile_span(sEnv, ni, kQBN, t_begin, t_end);
@@ -548,8 +544,8 @@ hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const vo
     hipLaunchKernelGGL(kern, dim3(Ukv.cap), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout),
-                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), P, Ukv.list,
-                       P.flags + kSlotKvUnits, H, func, nfunc, alpha, scale, pstore);
+                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), P, Ukv.list, H,
+                       func, nfunc, alpha, scale, pstore);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -559,8 +555,7 @@ hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const vo
     hipLaunchKernelGGL(k_bwd_q, dim3(Uq.cap), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout),
-                       static_cast<uint16_t*>(dq), P, Uq.list, P.flags + kSlotQUnits, H, func,
-                       nfunc, alpha, scale);
+                       static_cast<uint16_t*>(dq), P, Uq.list, H, func, nfunc, alpha, scale);
   }
   return hipGetLastError();
 }

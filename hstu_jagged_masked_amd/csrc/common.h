@@ -14,7 +14,10 @@
 //   unit       one workgroup's work item {b, tile, h}; unit lists are built on
 //              the device, sequences ordered longest first and dealt across the
 //              8 XCDs so each XCD gets a balanced share and keeps a sequence's
-//              tiles (which re-read the same K/V) in its own L2.
+//              tiles (which re-read the same K/V) in its own L2.  The list is
+//              indexed by workgroup and each record also carries the
+//              sequence's start, length, first row block and stored-P base, so
+//              a workgroup's first load is its whole unit.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -62,8 +65,17 @@ struct Prep {
 };
 
 struct Units {
-  int4* list;  // {b, tile, h, 0}; b < 0 marks an unused slot
-  int cap;     // entries (multiple of 8)
+  int4* list;  // 2 int4 per workgroup: {b, tile, h, L}, {s, rb_off[b], pblk[b] lo, hi};
+               // b < 0 marks an idle workgroup
+  int cap;     // workgroups (multiple of 8)
+};
+
+// One workgroup's unit, decoded from its record (all fields wave-uniform).
+struct UnitRec {
+  int b, tile, h, L;
+  int64_t s;     // first row of the sequence
+  int rb;        // first row block of the sequence
+  int64_t pblk;  // stored-P blocks before the sequence (per head), 0 if not planned
 };
 
 // ---------------------------------------------------------------------------
@@ -166,12 +178,27 @@ __device__ __forceinline__ int xcd_slot(int bid, int n) {
 }
 
 // Values every lane of the wave holds in common, moved to scalar registers.
+
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 __device__ __forceinline__ int64_t uniform(int64_t x) {
   const uint64_t u = (uint64_t)x;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
   return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The unit of workgroup blockIdx.x; false for an idle workgroup.
+__device__ __forceinline__ bool unit_of_block(const int4* __restrict__ list, UnitRec& u) {
+  const int4 a = list[2 * (int64_t)blockIdx.x];
+  const int4 c = list[2 * (int64_t)blockIdx.x + 1];
+  u.b = uniform(a.x);
+  u.tile = uniform(a.y);
+  u.h = uniform(a.z);
+  u.L = uniform(a.w);
+  u.s = (int64_t)uniform(c.x);
+  u.rb = uniform(c.y);
+  u.pblk = (int64_t)(((uint64_t)(uint32_t)uniform(c.w) << 32) | (uint32_t)uniform(c.z));
+  return u.b >= 0;
 }
 
 // Largest index i in [0, n] with a[i] <= x (a nondecreasing, a[0] <= x).

@@ -39,16 +39,14 @@ using S1 = std::integral_constant<int, 1>;
 
 __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
     const uint16_t* __restrict__ k, uint16_t* __restrict__ dq, Prep P,
-    const int4* __restrict__ units, const int* __restrict__ unit_count, int H, int nfunc,
-    const uint16_t* __restrict__ pstore, float out_scale) {
+    const int4* __restrict__ units, int H, int nfunc, const uint16_t* __restrict__ pstore,
+    float out_scale) {
   __shared__ __attribute__((aligned(256))) uint16_t sK0[kKStage], sK1[kKStage];
 
-  const int slot = xcd_slot(blockIdx.x, *unit_count);
-  if (slot < 0) return;
-  const int4 u = units[slot];
-  const int b = uniform(u.x), qt = uniform(u.y), h = uniform(u.z);
-  const int64_t s = uniform(P.so[b]);
-  const int L = uniform((int)(P.so[b + 1] - s));
+  UnitRec u;
+  if (!unit_of_block(units, u)) return;
+  const int qt = u.tile, h = u.h, L = u.L;
+  const int64_t s = u.s;
   const int r0 = qt * kBM;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -61,7 +59,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
   const int q0 = r0 + wave * kStep;
   const bool wave_rows = q0 < L;
   const int nrb = (L + kRB - 1) / kRB;
-  const int4* env = P.env + (int64_t)P.rb_off[b] * ni;
+  const int4* env = P.env + (int64_t)u.rb * ni;
   const int rb_a = r0 / kRB, rb_b = rb_a + 1;  // the workgroup's two row blocks
   const bool has_b = rb_b < nrb;
   const bool in_b = wave >= 2;                 // waves 2, 3 own rows of the second
@@ -121,7 +119,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
 
   const int64_t nkt = (L + kKT - 1) / kKT, nsteps = (L + kStep - 1) / kStep;
   // this wave's stored-P blocks: the kt-th at pw + kt * nsteps * 4096 elements
-  const uint16_t* pw = pstore + ((P.pblk[b] * H + h * nkt * nsteps + q0 / kStep) << 12) + lane * 8;
+  const uint16_t* pw = pstore + ((u.pblk * H + h * nkt * nsteps + q0 / kStep) << 12) + lane * 8;
   const uint16_t* kh = k + s * rs + (int64_t)h * kD;
 
   int kdoff[kKDma];
@@ -260,8 +258,8 @@ hipError_t launch_dq_from_p(const void* k, void* dq, const Prep& P, const Units&
   if (Uq.cap == 0) return hipSuccess;
   ProfScope ps(stream, "k_bwd_dq");
   hipLaunchKernelGGL(k_bwd_dq, dim3(Uq.cap), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(k), static_cast<uint16_t*>(dq), P, Uq.list,
-                     P.flags + kSlotQUnits, H, nfunc, pstore, out_scale);
+                     static_cast<const uint16_t*>(k), static_cast<uint16_t*>(dq), P, Uq.list, H,
+                     nfunc, pstore, out_scale);
   return hipGetLastError();
 }
 

@@ -50,8 +50,7 @@ static_assert(kKInstr <= 4 * kDmaPerWave && kVInstr <= 4 * kDmaPerWave, "DMA spl
 __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, Prep P, const int4* __restrict__ units,
-    const int* __restrict__ unit_count, int H, const int32_t* __restrict__ func, int nfunc,
-    float alpha, float out_scale) {
+    int H, const int32_t* __restrict__ func, int nfunc, float alpha, float out_scale) {
   // two LDS stages as separate objects, so the compiler sees that the DMA
   // filling one stage does not alias the reads of the other
   __shared__ __attribute__((aligned(16))) uint16_t sK0[kKStage], sK1[kKStage];
@@ -60,12 +59,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
   __shared__ int sCount[2];
   __shared__ Envelope sEnv;
 
-  const int slot = xcd_slot(blockIdx.x, *unit_count);
-  if (slot < 0) return;
-  const int4 u = units[slot];
-  const int b = uniform(u.x), qt = uniform(u.y), h = uniform(u.z);
-  const int64_t s = uniform(P.so[b]);
-  const int L = uniform((int)(P.so[b + 1] - s));
+  UnitRec u;
+  if (!unit_of_block(units, u)) return;
+  const int qt = u.tile, h = u.h, L = u.L;
+  const int64_t s = u.s;
   const int r0 = qt * kBM;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -92,7 +89,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
     if (j < ni && row_ok) row_interval(func, P.total, s + row, j, L, lo[j], hi[j]);
   }
 
-  if (tid == 0) rows_envelope(P, b, r0, kBM, L, ni, sEnv);
+  if (tid == 0) rows_envelope(P, u.rb, r0, kBM, L, ni, sEnv);
   __syncthreads();
   int t_begin, t_end;
   envelope_tile_span(sEnv, ni, kBN, t_begin, t_end);
@@ -242,8 +239,8 @@ hipError_t launch_mfma_fwd(const void* q, const void* k, const void* v, void* o,
   ProfScope ps(stream, "k_fwd_bf16");
   hipLaunchKernelGGL(k_fwd_bf16, dim3(U.cap), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), P, U.list,
-                     P.flags + kSlotFwdUnits, H, func, nfunc, alpha, alpha * inv_max_len);
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), P, U.list, H,
+                     func, nfunc, alpha, alpha * inv_max_len);
   return hipGetLastError();
 }
 

@@ -188,18 +188,23 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prep P, const int64_t* __
   }
 }
 
-// Unit list for tiles of `tile` rows: sequence p (dealt order) owns the slots
-// [H*T[p], H*T[p+1]); within it head-major, tiles in decreasing index when
-// `descending` (heaviest first for prefix-like masks), else increasing.
+// Unit list for tiles of `tile` rows, one record per workgroup.  Unit lam
+// (in list order: sequence p of the dealt order owns [H*T[p], H*T[p+1]);
+// within it head-major, tiles in decreasing index when `descending`, heaviest
+// first for prefix-like masks, else increasing) runs on the workgroup that
+// xcd_slot maps to lam, so each XCD takes a contiguous share of the list.
 __global__ void k_units(Prep P, Units U, int tile, int descending, int H, int count_slot) {
-  const int lam = blockIdx.x * blockDim.x + threadIdx.x;
+  const int bid = blockIdx.x * blockDim.x + threadIdx.x;
   const int* T = tile == 64 ? P.tiles64 : P.tiles128;
   const int B = P.B;
   const int n = H * T[B];
-  if (lam == 0) P.flags[count_slot] = n;
-  if (lam >= U.cap) return;
-  if (lam >= n) {
-    U.list[lam] = make_int4(-1, 0, 0, 0);
+  if (bid == 0) P.flags[count_slot] = n;
+  if (bid >= U.cap) return;
+  const int lam = xcd_slot(bid, n);
+  int4* rec = U.list + 2 * (int64_t)bid;
+  if (lam < 0) {
+    rec[0] = make_int4(-1, 0, 0, 0);
+    rec[1] = make_int4(0, 0, 0, 0);
     return;
   }
   const int p = upper_index(T, B, lam / H);
@@ -207,7 +212,11 @@ __global__ void k_units(Prep P, Units U, int tile, int descending, int H, int co
   const int r = lam - H * T[p];
   const int h = r / nt;
   const int tr = r - h * nt;
-  U.list[lam] = make_int4(P.order[p], descending ? nt - 1 - tr : tr, h, 0);
+  const int b = P.order[p];
+  const int64_t s = P.so[b];
+  const int64_t pb = P.pblk ? P.pblk[b] : 0;
+  rec[0] = make_int4(b, descending ? nt - 1 - tr : tr, h, (int)(P.so[b + 1] - s));
+  rec[1] = make_int4((int)s, P.rb_off[b], (int)(uint32_t)(uint64_t)pb, (int)(uint32_t)((uint64_t)pb >> 32));
 }
 
 // One wave per row block: envelopes of every interval.

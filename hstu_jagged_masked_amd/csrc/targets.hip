@@ -77,20 +77,20 @@ struct Candidate {
 
 // Common unit decoding.  Returns false if this wave has no chunk.
 struct ChunkCtx {
-  int b, h, chunk, L, cand;
+  int b, h, chunk, L, cand, rb;
   int64_t s;
 };
 
-__device__ __forceinline__ bool chunk_ctx(const Prep& P, const int4* units, const int* count,
-                                          const int32_t* target_rows, ChunkCtx& C) {
-  const int slot = xcd_slot(blockIdx.x, *count);
-  if (slot < 0) return false;
-  const int4 u = units[slot];
-  C.b = u.x;
-  C.h = u.z;
-  C.s = P.so[C.b];
-  C.L = (int)(P.so[C.b + 1] - C.s);
-  C.chunk = u.y * kWaves + (int)(threadIdx.x >> 6);
+__device__ __forceinline__ bool chunk_ctx(const int4* units, const int32_t* target_rows,
+                                          ChunkCtx& C) {
+  UnitRec u;
+  if (!unit_of_block(units, u)) return false;
+  C.b = u.b;
+  C.h = u.h;
+  C.s = u.s;
+  C.L = u.L;
+  C.rb = u.rb;
+  C.chunk = u.tile * kWaves + (int)(threadIdx.x >> 6);
   if (C.chunk * kChunk >= C.L) return false;
   C.cand = min(max((int)target_rows[C.b], 0), C.L - 1);
   return true;
@@ -100,12 +100,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(64 * kWaves) void k_targets_fwd(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     float* __restrict__ partial, Prep P, const int4* __restrict__ units,
-    const int* __restrict__ count, int H, const int32_t* __restrict__ func, int nfunc,
+    int H, const int32_t* __restrict__ func, int nfunc,
     float alpha, const int32_t* __restrict__ target_rows) {
   using V = Vec16<T>;
   constexpr int VEC = V::N, LPR = D / VEC, RPW = 64 / LPR;
   ChunkCtx C;
-  if (!chunk_ctx(P, units, count, target_rows, C)) return;
+  if (!chunk_ctx(units, target_rows, C)) return;
   const int lane = threadIdx.x & 63;
   const int sub = lane % LPR, rg = lane / LPR;
   const int ni = (nfunc + 1) / 2;
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_targets_fwd(
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], m, 64);
   if (rg == 0) {
-    float* dst = partial + ((int64_t)(P.rb_off[C.b] + C.chunk) * H + C.h) * D + sub * VEC;
+    float* dst = partial + ((int64_t)(C.rb + C.chunk) * H + C.h) * D + sub * VEC;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) dst[e] = acc[e];
   }
@@ -160,12 +160,12 @@ __global__ __launch_bounds__(64 * kWaves) void k_targets_bwd(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, T* __restrict__ dk, T* __restrict__ dv,
     float* __restrict__ partial, Prep P, const int4* __restrict__ units,
-    const int* __restrict__ count, int H, const int32_t* __restrict__ func, int nfunc,
+    int H, const int32_t* __restrict__ func, int nfunc,
     float alpha, float out_scale, const int32_t* __restrict__ target_rows) {
   using V = Vec16<T>;
   constexpr int VEC = V::N, LPR = D / VEC, RPW = 64 / LPR;
   ChunkCtx C;
-  if (!chunk_ctx(P, units, count, target_rows, C)) return;
+  if (!chunk_ctx(units, target_rows, C)) return;
   const int lane = threadIdx.x & 63;
   const int sub = lane % LPR, rg = lane / LPR;
   const int ni = (nfunc + 1) / 2;
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_targets_bwd(
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], m, 64);
   if (rg == 0) {
-    float* dst = partial + ((int64_t)(P.rb_off[C.b] + C.chunk) * H + C.h) * D + sub * VEC;
+    float* dst = partial + ((int64_t)(C.rb + C.chunk) * H + C.h) * D + sub * VEC;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) dst[e] = acc[e];
   }
@@ -259,8 +259,8 @@ hipError_t fwd_impl(const void* q, const void* k, const void* v, void* o, const 
   if (U.cap > 0) {
     ProfScope ps(stream, "k_targets_fwd");
     hipLaunchKernelGGL((k_targets_fwd<T, D>), dim3(U.cap), dim3(64 * kWaves), 0, stream,
-                       (const T*)q, (const T*)k, (const T*)v, partial, P, U.list,
-                       P.flags + kSlotFwdUnits, H, func, nfunc, alpha, target_rows);
+                       (const T*)q, (const T*)k, (const T*)v, partial, P, U.list, H,
+                       func, nfunc, alpha, target_rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -279,8 +279,7 @@ hipError_t bwd_impl(const void* q, const void* k, const void* v, const void* dou
     ProfScope ps(stream, "k_targets_bwd");
     hipLaunchKernelGGL((k_targets_bwd<T, D>), dim3(U.cap), dim3(64 * kWaves), 0, stream,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)dout, (T*)dk, (T*)dv,
-                       partial, P, U.list, P.flags + kSlotFwdUnits, H, func, nfunc, alpha, scale,
-                       target_rows);
+                       partial, P, U.list, H, func, nfunc, alpha, scale, target_rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -40,11 +40,11 @@ struct Envelope {
   int ulo[kMaxNI], uhi[kMaxNI], ilo[kMaxNI], ihi[kMaxNI];
 };
 
-__device__ __forceinline__ void rows_envelope(const Prep& P, int b, int r0, int rows, int L,
+__device__ __forceinline__ void rows_envelope(const Prep& P, int rb_seq, int r0, int rows, int L,
                                               int ni, Envelope& E) {
   const int rb0 = r0 / kRB;
   const int nrb = min((rows + kRB - 1) / kRB, (L - r0 + kRB - 1) / kRB);
-  const int4* env = P.env + (int64_t)(P.rb_off[b] + rb0) * ni;
+  const int4* env = P.env + (int64_t)(rb_seq + rb0) * ni;
 #pragma unroll
   for (int j = 0; j < kMaxNI; ++j) {
     E.ulo[j] = L;
