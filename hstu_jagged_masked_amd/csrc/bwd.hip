@@ -279,18 +279,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
         p_pending = q0 + hf * kKvBM;
       }
       // dV^T += dO^T Y and dK^T += Q^T P: A operands by transpose reads, query
-      // rows 16hh + 4g + {0..3} and 16hh + 8 + 4g + {0..3}
+      // rows 16hh + 4g + {0..3} and 16hh + 8 + 4g + {0..3}; the operands of
+      // step o + 1 (o = 4 hh + mb) are read before the products of step o so
+      // that the LDS latency is not waited for right before each product
+      auto ld = [&](int o, bf16x8& ag, bf16x8& aq) {
+        const int hh = o >> 2, mb = o & 3;
+        const int o0 = (tr_b ^ (64 * mb)) + 16 * hh * 256;
+        const int o1 = (tr_b ^ (64 * mb) ^ 32) + (16 * hh + 8) * 256;
+        ag = concat4(lds_tr8(sG, o0), lds_tr8(sG, o1));
+        aq = concat4(lds_tr8(sQ, o0), lds_tr8(sQ, o1));
+      };
+      bf16x8 ag0, aq0, ag1, aq1;
+      ld(0, ag0, aq0);
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int mb = 0; mb < kD / 32; ++mb) {
-          const int o0 = (tr_b ^ (64 * mb)) + 16 * hh * 256;
-          const int o1 = (tr_b ^ (64 * mb) ^ 32) + (16 * hh + 8) * 256;
-          const bf16x8 ag = concat4(lds_tr8(sG, o0), lds_tr8(sG, o1));
-          dvacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, yb[hh], dvacc[mb], 0, 0, 0);
-          const bf16x8 aq = concat4(lds_tr8(sQ, o0), lds_tr8(sQ, o1));
-          dkacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, pb[hh], dkacc[mb], 0, 0, 0);
+      for (int o = 0; o < 8; ++o) {
+        const int hh = o >> 2, mb = o & 3;
+        if (o + 1 < 8) {
+          if (o & 1)
+            ld(o + 1, ag0, aq0);
+          else
+            ld(o + 1, ag1, aq1);
         }
+        const bf16x8 ag = (o & 1) ? ag1 : ag0, aq = (o & 1) ? aq1 : aq0;
+        dvacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, yb[hh], dvacc[mb], 0, 0, 0);
+        dkacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, pb[hh], dkacc[mb], 0, 0, 0);
       }
     }
   };
