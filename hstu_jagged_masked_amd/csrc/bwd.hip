@@ -452,18 +452,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
     const uint16_t* sV = st ? sV1 : sV0;
     const int rd_b = opaque(rd_b0), tr_b = opaque(tr_b0);
     f32x16 sacc[2], dsacc[2];
+    // operands of (kb, ks) step o = 8 kb + ks read one step ahead
+    auto ldr = [&](int o, bf16x8& a, bf16x8& b) {
+      const int off = (rd_b ^ (32 * (o & 7))) + (o >> 3) * 32 * 256;
+      a = lds_row16(sK, off);
+      b = lds_row16(sV, off);
+    };
+    bf16x8 ra0, rb0, ra1, rb1;
+    ldr(0, ra0, rb0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
-      dsacc[kb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) {
-        const int off = (rd_b ^ (32 * ks)) + kb * 32 * 256;
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row16(sK, off), qf[ks], sacc[kb],
-                                                           0, 0, 0);
-        dsacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row16(sV, off), gf[ks],
-                                                            dsacc[kb], 0, 0, 0);
+    for (int o = 0; o < 16; ++o) {
+      const int kb = o >> 3, ks = o & 7;
+      if (ks == 0) {
+        sacc[kb] = f32x16{};
+        dsacc[kb] = f32x16{};
       }
+      if (o + 1 < 16) {
+        if (o & 1)
+          ldr(o + 1, ra0, rb0);
+        else
+          ldr(o + 1, ra1, rb1);
+      }
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((o & 1) ? ra1 : ra0, qf[ks], sacc[kb], 0,
+                                                         0, 0);
+      dsacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((o & 1) ? rb1 : rb0, gf[ks], dsacc[kb],
+                                                          0, 0, 0);
     }
     bf16x8 pb[4];
 #pragma unroll
@@ -484,15 +497,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
     }
+    auto ldk = [&](int o) {
+      const int ss = o >> 2, mb = o & 3;
+      const int o0 = (tr_b ^ (64 * mb)) + 16 * ss * 256;
+      const int o1 = (tr_b ^ (64 * mb) ^ 32) + (16 * ss + 8) * 256;
+      return concat4(lds_tr8(sK, o0), lds_tr8(sK, o1));
+    };
+    bf16x8 ka0 = ldk(0), ka1;
 #pragma unroll
-    for (int ss = 0; ss < 4; ++ss) {
-#pragma unroll
-      for (int mb = 0; mb < kD / 32; ++mb) {
-        const int o0 = (tr_b ^ (64 * mb)) + 16 * ss * 256;
-        const int o1 = (tr_b ^ (64 * mb) ^ 32) + (16 * ss + 8) * 256;
-        const bf16x8 a = concat4(lds_tr8(sK, o0), lds_tr8(sK, o1));
-        dqacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ss], dqacc[mb], 0, 0, 0);
+    for (int o = 0; o < 16; ++o) {
+      if (o + 1 < 16) {
+        if (o & 1)
+          ka0 = ldk(o + 1);
+        else
+          ka1 = ldk(o + 1);
       }
+      dqacc[o & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((o & 1) ? ka1 : ka0, pb[o >> 2],
+                                                             dqacc[o & 3], 0, 0, 0);
     }
   };
 
