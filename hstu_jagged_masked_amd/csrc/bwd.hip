@@ -169,7 +169,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
       for (int ksl = 0; ksl < 2; ++ksl) {
         const bf16x8 t = concat4(lds_tr8(p_stage, p_tr + ksl * 16 * 64),
                                  lds_tr8(p_stage, p_tr + (ksl * 16 + 4) * 64));
-        *reinterpret_cast<bf16x8*>(blk + (2 * wave + ksl) * 512) = t;
+        // written once and read back by the dQ pass long after it has left
+        // L2: a non-temporal store keeps the Q / dO tiles cached instead
+        __builtin_nontemporal_store(t, reinterpret_cast<bf16x8*>(blk + (2 * wave + ksl) * 512));
       }
       p_pending = -1;
     }

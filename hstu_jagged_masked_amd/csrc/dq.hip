@@ -134,10 +134,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
     for (int i = 0; i < kKDma; ++i)
       lds_dma16_raw(rk, (st ? sK1 : sK0) + (wave + 4 * i) * 512, kdoff[i]);
   };
+  // P is read exactly once: non-temporal loads, so that it does not push the
+  // K tiles (re-read by every query block of the sequence) out of L2
   auto load_p = [&](int kt, bf16x8* dst) {
     const uint16_t* src = pw + (((int64_t)kt * nsteps) << 12);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) dst[ks] = *reinterpret_cast<const bf16x8*>(src + ks * 512);
+    for (int ks = 0; ks < kKSteps; ++ks)
+      dst[ks] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(src + ks * 512));
   };
 
   // K^T transpose reads: lane j of 16-lane group G takes key rows 8*(G/2) + j/4
