@@ -216,15 +216,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     constexpr int st = decltype(stage)::value;
     const int nh = q0 + kKvBM < L ? 2 : 1;  // halves of 32 rows in this step
     if constexpr (kMasked) {
-      // rows q0 + 32 hf + n: visibility of this wave's 32 key columns
-      // (wave-private LDS), before the next step's copies so the func loads
-      // do not wait behind them
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        int lo[kMaxNI], hi[kMaxNI];
-        row_intervals_rsrc(fseq, P.total, q0 + hf * kKvBM + n, ni, L, lo, hi);
-        if (g == 0) sMask[wave][hf * kKvBM + n] = col_mask32(lo, hi, ni, c0 + wave * 32);
-      }
+      // row q0 + 32 g + n (lane (n, g) takes one row of half g): visibility of
+      // this wave's 32 key columns (wave-private LDS), before the next step's
+      // copies so the func loads do not wait behind them
+      int lo[kMaxNI], hi[kMaxNI];
+      row_intervals_rsrc(fseq, P.total, q0 + g * kKvBM + n, ni, L, lo, hi);
+      sMask[wave][g * kKvBM + n] = col_mask32(lo, hi, ni, c0 + wave * 32);
     }
     if (next >= 0) {
       if constexpr (st == 0) {
