@@ -10,10 +10,12 @@ hstu_attn_bwd over the whole batch.
 
 Reported ("value"): effective TFLOP/s = 14 * D * H * sum_i |V_i| / step time,
 counting 4*D (forward) + 10*D (backward) flops per visible (query, key) pair and
-head, over unmasked pairs only.  Also reported: the targets-only mode (one
-candidate row per sequence against full-length K/V), per-kernel times measured
-with HIP events on the launch stream during the timed steps, the roofline of
-the dominant kernel, and the fp64 CPU oracle's rate on a sample of sequences.
+head, over unmasked pairs only.  Also reported: per-step median and minimum
+over 3 further runs and the spread of their medians (step_stats), the
+targets-only mode (one candidate row per sequence against full-length K/V),
+per-kernel times measured with HIP events on the launch stream during the
+timed steps, the roofline of the dominant kernel, and the fp64 CPU oracle's
+rate on a sample of sequences.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -133,6 +135,27 @@ def split_ms(hj, torch, t, cfg, steps, pstore):
     return out
 
 
+def step_stats(hj, torch, t, cfg, steps, runs, pstore):
+    """Per-step fwd+bwd times (a HIP event pair around each step), `runs`
+    runs of `steps` steps after the timed region: median and min of each run
+    and the spread of the run medians."""
+    per_run = []
+    for _ in range(runs):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(steps):
+            run_steps(hj, t, cfg, 1, pstore=pstore)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per_run.append([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    med = [float(np.median(r)) for r in per_run]
+    return {"runs": runs, "steps_per_run": steps,
+            "median_ms": [round(m, 4) for m in med],
+            "min_ms": [round(min(r), 4) for r in per_run],
+            "spread_pct": round(100.0 * (max(med) - min(med)) / min(med), 2)}
+
+
 def cpu_baseline(cfg, t, off, nseq):
     """The fp64 oracle on the first `nseq` sequences (fwd + bwd), host cores."""
     import oracle
@@ -217,6 +240,7 @@ def main():
     ms, wall, prof = timed(hj, torch, t, cfg, args.steps, pstore=pstore)
     log(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step")
     split = split_ms(hj, torch, t, cfg, args.steps, pstore)
+    stats = step_stats(hj, torch, t, cfg, args.steps, 3, pstore)
     flops_eff = 14.0 * D * H * pairs
     value = flops_eff / (ms * 1e-3) / 1e12
 
@@ -299,6 +323,7 @@ def main():
         # the same step counted at 12*D per pair (no recomputed products)
         "value_12d": round(12.0 * D * H * pairs / (ms * 1e-3) / 1e12, 2),
         "split_ms": split,
+        "step_stats": stats,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "targets_only": targets,
