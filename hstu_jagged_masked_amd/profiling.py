@@ -61,20 +61,37 @@ def read_rows(path_glob):
 
 
 def stats(directory: str) -> str:
-    rows = read_rows(os.path.join(directory, "**", "*kernel_stats.csv"))
-    out = ["kernel                     calls   avg_ms      total_ms   pct"]
+    """Per-kernel durations from the kernel trace, one line per (kernel, grid
+    size): the production workload and the smaller ones bench.py also runs
+    (the padded-interval comparison) launch the same kernels on other grids."""
+    rows = read_rows(os.path.join(directory, "**", "*kernel_trace.csv"))
+    groups = collections.defaultdict(list)
     for r in rows:
-        name = short_name(r["Name"])
-        out.append(f"{name:26s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e6:9.4f} "
-                   f"{float(r['TotalDurationNs']) / 1e6:11.3f} {float(r['Percentage']):6.2f}")
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        groups[(short_name(r["Kernel_Name"]), grid)].append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    total = sum(sum(v) for v in groups.values())
+    out = ["kernel                        grid  calls   avg_ms      total_ms   pct"]
+    for (name, grid), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"{name[:26]:26s} {grid:8d} {len(ds):6d} {sum(ds) / len(ds):9.4f} "
+                   f"{sum(ds):11.3f} {100.0 * sum(ds) / total:6.2f}")
     return "\n".join(out)
 
 
-def pmc_table(directories):
-    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+def pmc_table(directories, largest_grid=True):
+    """Counter values per kernel name; with largest_grid, only the dispatches
+    on each kernel's largest grid (the production workload)."""
+    rows = []
     for d in directories:
-        for r in read_rows(os.path.join(d, "**", "*counter_collection.csv")):
-            agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        rows.extend(read_rows(os.path.join(d, "**", "*counter_collection.csv")))
+    top = collections.defaultdict(int)
+    for r in rows:
+        top[r["Kernel_Name"]] = max(top[r["Kernel_Name"]], int(r["Grid_Size"]))
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in rows:
+        if largest_grid and int(r["Grid_Size"]) != top[r["Kernel_Name"]]:
+            continue
+        agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
     return agg
 
 
