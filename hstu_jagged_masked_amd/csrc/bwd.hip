@@ -82,18 +82,18 @@ __device__ __forceinline__ void step_window(const int4* env, int ni, int L, int 
   n_full = __popcll(mf);
 }
 
-// kStoreP: also store each step's P (bf16, as rounded for the dK product) for
-// the dQ pass.  Layout, per (sequence, head): blocks [128-key tile kt][32-row
-// step] of 8 KiB, block (kt, step) at ((pblk[b] H + h nkt nsteps) + kt nsteps
-// + step) * 8 KiB.  A block is the B operand of dQ^T += K^T P^T, ready to
-// load: [key step ks of 16 keys][lane l][8 bf16], lane l holding the keys
-// 16 ks + 8 (l/32) + 0..7 of row position l%32, where row position
-// hh*16 + g*8 + e is query row (2 hh + e/4)*8 + g*4 + e%4 of the step (the
-// order of the registers pb[hh][e] of lane (key, g)).  The transpose goes
-// through a wave-private LDS buffer, and a step's stores are issued at the
-// start of the next step so that they have landed by the barrier after it
-// (stores and loads share vmcnt).  Only the steps a key tile walks are
-// written; the dQ pass reads exactly those.
+// kStoreP: also store each half's P (bf16, as rounded for the dK product)
+// for the dQ pass.  Layout, per (sequence, head): blocks [128-key tile
+// kt][32-row half t] of 8 KiB, block (kt, t) at ((pblk[b] H + h nkt nsteps)
+// + kt nsteps + t) * 8 KiB with nsteps = ceil(L/32).  A block is the B
+// operand of dQ^T += K^T P^T, ready to load: [key step ks of 16 keys][lane
+// l][8 bf16], lane l holding the keys 16 ks + 8 (l/32) + 0..7 of row position
+// l%32, where row position hh*16 + g*8 + e is query row (2 hh + e/4)*8 + g*4
+// + e%4 of the half (the order of the registers pb[hh][e] of lane (key, g)).
+// The transpose goes through a wave-private LDS buffer, and a half's stores
+// are issued at the start of the next half, so that they are well on their
+// way by the next barrier (stores and loads share vmcnt).  Only the halves a
+// key tile walks are written; the dQ pass reads exactly those.
 template <bool kStoreP>
 __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,

@@ -6,8 +6,8 @@
 // and stored it (masked pairs hold 0).  No S, dS or mask is recomputed here.
 //
 // One workgroup (4 waves) owns 128 query rows of one (sequence, head); wave w
-// owns the 32-row step r0 + 32w.  The workgroup walks the 128-key tiles its
-// row blocks reach.  Per tile:
+// owns the 32 rows from r0 + 32w (one stored-P half).  The workgroup walks
+// the 128-key tiles its row blocks reach.  Per tile:
 //   * the K rows -> LDS (swizzled 256-byte rows) by buffer-to-LDS copies into
 //     one of two stages, the next tile's copy in flight during this tile;
 //   * each wave's stored P block (8 KiB, already in the B-operand layout of

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prep P, const int64_t* __
     carry64 += t64;
     carry128 += t128;
     if (P.pblk) {
-      // stored-P blocks of one head: (128-key tiles) x (32-row steps)
+      // stored-P blocks of one head: (128-key tiles) x (32-row halves)
       int64_t nblk = 0;
       if (b < B) {
         const int L = (int)(P.so[b + 1] - P.so[b]);
