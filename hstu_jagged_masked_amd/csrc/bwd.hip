@@ -85,15 +85,14 @@ __device__ __forceinline__ void step_window(const int4* env, int ni, int L, int 
 // kStoreP: also store each half's P (bf16, as rounded for the dK product)
 // for the dQ pass.  Layout, per (sequence, head): blocks [128-key tile
 // kt][32-row half t] of 8 KiB, block (kt, t) at ((pblk[b] H + h nkt nsteps)
-// + kt nsteps + t) * 8 KiB with nsteps = ceil(L/32).  A block is the B
-// operand of dQ^T += K^T P^T, ready to load: [key step ks of 16 keys][lane
-// l][8 bf16], lane l holding the keys 16 ks + 8 (l/32) + 0..7 of row position
-// l%32, where row position hh*16 + g*8 + e is query row (2 hh + e/4)*8 + g*4
-// + e%4 of the half (the order of the registers pb[hh][e] of lane (key, g)).
-// The transpose goes through a wave-private LDS buffer, and a half's stores
-// are issued at the start of the next half, so that they are well on their
-// way by the next barrier (stores and loads share vmcnt).  Only the halves a
-// key tile walks are written; the dQ pass reads exactly those.
+// + kt nsteps + t) * 8 KiB with nsteps = ceil(L/32).  A block holds the
+// registers pb[hh] of the four waves as they are: [wave w][hh][lane (n, g)][8
+// bf16], i.e. key 32 w + n at row positions hh*16 + g*8 + 0..7, where row
+// position hh*16 + g*8 + e is query row (2 hh + e/4)*8 + g*4 + e%4 of the
+// half.  The dQ pass transposes it.  Each half's stores go out as soon as its
+// P is formed (holding the second half's until after the next barrier
+// measured the same).  Only the halves a key tile walks are written; the dQ
+// pass reads exactly those.
 template <bool kStoreP>
 __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -108,8 +107,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   __shared__ __attribute__((aligned(16))) uint32_t sMask[4][kStepRows];
   __shared__ int sPart[kStepWin], sFull[kStepWin];
   __shared__ int sCount[2];
-  // P staging: per wave [32 keys][32 row positions], 64-byte rows
-  __shared__ __attribute__((aligned(16))) uint16_t sPst[kStoreP ? 4 * 1024 : 8];
 
   UnitRec u;
   if (!unit_of_block(units, u)) return;
@@ -147,34 +144,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
 
   const uint16_t* qh = q + s * rs + (int64_t)h * kD;
   const uint16_t* gh = dout + s * rs + (int64_t)h * kD;
-  // stored P: this workgroup's first block (uniform); the staged step
+  // stored P: this workgroup's first block (uniform)
   int64_t p_blk0 = 0;
-  int p_pending = -1;  // first row of the step whose P sits in sPst, or -1
   if constexpr (kStoreP) {
     const int64_t nkt = (L + kKvBN - 1) / kKvBN, nsteps = (L + kKvBM - 1) / kKvBM;
     p_blk0 = u.pblk * H + h * nkt * nsteps + kt * nsteps;
   }
-  uint16_t* const p_stage = sPst + (kStoreP ? wave * 1024 : 0);
-  // transpose reads of the staging rows: lane j of 16-lane group G reads key
-  // row 8*(G/2) + j/4 (+ 16 ksl, + 4 for the second read), row positions
-  // (G%2)*16 + 4*(j%4)..+3; lane l then holds keys 16 ksl + 8 (l/32) + 0..7 of
-  // row position l%32
-  const int p_tr = (8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * 64 +
-                   (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
-  auto p_flush = [&]() {
-    if constexpr (kStoreP) {
-      if (p_pending < 0) return;
-      uint16_t* blk = pstore + ((p_blk0 + p_pending / kKvBM) << 12) + lane * 8;
-#pragma unroll
-      for (int ksl = 0; ksl < 2; ++ksl) {
-        const bf16x8 t = concat4(lds_tr8(p_stage, p_tr + ksl * 16 * 64),
-                                 lds_tr8(p_stage, p_tr + (ksl * 16 + 4) * 64));
-        // written once and read back by the dQ pass long after it has left
-        // L2: a non-temporal store keeps the Q / dO tiles cached instead
-        __builtin_nontemporal_store(t, reinterpret_cast<bf16x8*>(blk + (2 * wave + ksl) * 512));
-      }
-      p_pending = -1;
-    }
+  // written once and read back by the dQ pass long after it has left L2:
+  // non-temporal stores keep the Q / dO tiles cached instead
+  auto p_store = [&](int r, const bf16x8* pv) {
+    uint16_t* blk = pstore + ((p_blk0 + r / kKvBM) << 12) + wave * 1024 + lane * 8;
+    __builtin_nontemporal_store(pv[0], reinterpret_cast<bf16x8*>(blk));
+    __builtin_nontemporal_store(pv[1], reinterpret_cast<bf16x8*>(blk + 512));
   };
   // DMA of one 64-row step: wave w issues instructions I = w + 4i of each
   // tensor; lane l of instruction I fills LDS slot 64*I + l
@@ -236,8 +217,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
       const uint16_t* sQ = (st ? sQ1 : sQ0) + hf * kKvBM * kD;
       const uint16_t* sG = (st ? sG1 : sG0) + hf * kKvBM * kD;
       const int rd_b = opaque(rd_b0), tr_b = opaque(tr_b0);
-      // the previous half's P
-      p_flush();
       f32x16 sacc = f32x16{}, dsacc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < kD / 16; ++ks) {
@@ -271,12 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
           pb[r >> 3][r & 7] = (__bf16)p;
         }
       }
-      if constexpr (kStoreP) {
-        // stage [key n][row position hh*16 + g*8 + e]; stored by the next half
-        *reinterpret_cast<bf16x8*>(p_stage + n * 32 + g * 8) = pb[0];
-        *reinterpret_cast<bf16x8*>(p_stage + n * 32 + 16 + g * 8) = pb[1];
-        p_pending = q0 + hf * kKvBM;
-      }
+      if constexpr (kStoreP) p_store(q0 + hf * kKvBM, pb);
       // dV^T += dO^T Y and dK^T += Q^T P: A operands by transpose reads, query
       // rows 16hh + 4g + {0..3} and 16hh + 8 + 4g + {0..3}; the operands of
       // step o + 1 (o = 4 hh + mb) are read before the products of step o so
@@ -337,7 +311,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     // the next window rewrites the lists and counts: every wave is done with them
     __syncthreads();
   }
-  p_flush();
 
   // epilogue: lane holds d = mb*32 + j*8 + g*4 + 0..3 of key row `col`
   if (col_ok) {

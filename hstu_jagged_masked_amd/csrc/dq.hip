@@ -10,8 +10,11 @@
 // the 128-key tiles its row blocks reach.  Per tile:
 //   * the K rows -> LDS (swizzled 256-byte rows) by buffer-to-LDS copies into
 //     one of two stages, the next tile's copy in flight during this tile;
-//   * each wave's stored P block (8 KiB, already in the B-operand layout of
-//     dQ^T += K^T P^T) -> registers by plain 16-byte loads, two tiles ahead;
+//   * each wave's stored P block (8 KiB, the key-owner kernel's registers as
+//     they were: key-major, 8 row positions per 16 bytes) -> registers by
+//     plain 16-byte loads, two tiles ahead;
+//   * P transposed through a wave-private LDS buffer, 32 keys at a time, into
+//     the B operand of dQ^T += K^T P^T (row position per lane, 8 keys);
 //   * dQ^T += K^T P^T on MFMA, A = K^T by LDS transpose reads.
 // A wave whose row block the key tile does not reach has no P block for it
 // and skips that tile.  The accumulator columns are P's row positions; the
@@ -42,6 +45,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
     const int4* __restrict__ units, int H, int nfunc, const uint16_t* __restrict__ pstore,
     float out_scale) {
   __shared__ __attribute__((aligned(256))) uint16_t sK0[kKStage], sK1[kKStage];
+  // per wave: P of 32 keys as [key][32 row positions], 64-byte rows, 16-byte
+  // chunk c of key row r at position c ^ ((r / 4) mod 4)
+  __shared__ __attribute__((aligned(16))) uint16_t sPt[4 * 32 * 32];
 
   UnitRec u;
   if (!unit_of_block(units, u)) return;
@@ -151,14 +157,43 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
   const int tr_b0 = trow * 256 + 8 * (gl & 1) +
                     ((((grp & 1) * 2 + ((gl & 3) >> 1)) ^ swz(trow)) << 4);
 
+  // P transpose.  Register j of a P block, lane (n, g), holds key 32 (j/2) + n
+  // at row positions (2 (j%2) + g) * 8 + 0..7: written to row n, chunk
+  // 2 (j%2) + g of the buffer.  Read back like K^T: lane j of 16-lane group G
+  // reads key rows 8*(G/2) + j/4 (+ 16 ksl; + 4 for the second read), row
+  // positions (G%2)*16 + 4*(j%4), so lane l holds keys 16 ks + 8 (l/32) + 0..7
+  // of row position l%32.  (Rows + 4 flip the chunk swizzle's low bit.)
+  char* const pbuf = reinterpret_cast<char*>(sPt + wave * 1024);
+  const int pw_b0 = n * 64 + ((g ^ ((n >> 2) & 3)) << 4);
+  const int pr_b0 = (8 * (grp >> 1) + (gl >> 2)) * 64 +
+                    ((((grp & 1) * 2 + ((gl & 3) >> 1)) ^ (2 * (grp >> 1))) << 4) +
+                    (gl & 1) * 8;
+  auto p_tr = [&](int off) {
+    return lds_read_tr(reinterpret_cast<const uint16_t*>(pbuf + off));
+  };
+
   f32x16 acc[kD / 32];
 #pragma unroll
   for (int mb = 0; mb < kD / 32; ++mb) acc[mb] = f32x16{};
 
-  auto compute = [&](const bf16x8* pt, auto stage) {
+  auto compute = [&](const bf16x8* pj, auto stage) {
     constexpr int st = decltype(stage)::value;
     const uint16_t* sK = st ? sK1 : sK0;
     const int tr_b = opaque(tr_b0);
+    const int pw_b = opaque(pw_b0), pr_b = opaque(pr_b0);
+    bf16x8 pt[kKSteps];
+#pragma unroll
+    for (int r = 0; r < kKT / 32; ++r) {
+      // (one wave's LDS operations run in order: this round's writes follow
+      // the previous round's reads)
+      *reinterpret_cast<bf16x8*>(pbuf + pw_b) = pj[2 * r];
+      *reinterpret_cast<bf16x8*>(pbuf + (pw_b ^ 32)) = pj[2 * r + 1];
+#pragma unroll
+      for (int ksl = 0; ksl < 2; ++ksl)
+        pt[2 * r + ksl] = __builtin_shufflevector(p_tr(pr_b + ksl * 1024),
+                                                  p_tr((pr_b ^ 16) + 256 + ksl * 1024), 0, 1,
+                                                  2, 3, 4, 5, 6, 7);
+    }
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
