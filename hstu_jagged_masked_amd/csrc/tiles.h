@@ -203,13 +203,14 @@ __device__ __forceinline__ void lds_barrier() {
 // caller orders it explicitly: s_waitcnt vmcnt plus a barrier before the
 // copied data is read, and a barrier before its destination is overwritten.
 // `lds` must be wave-uniform.  M0 is set here; no other code in these kernels
-// keeps a value in M0.
+// keeps a value in M0.  A copy into LDS that reads M0 needs one wait state
+// after the write to M0 (the compiler cannot see inside the assembly to add it).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16_raw(__amdgpu_buffer_rsrc_t r, const void* lds,
                                               int voffset) {
   const int m0 = __builtin_amdgcn_readfirstlane((int)(uintptr_t)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0),
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0),
                "v"(voffset), "s"(r)
                : "memory", "m0");
 }
