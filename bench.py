@@ -187,7 +187,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="hstu_2663", choices=wl.WORKLOADS)
     ap.add_argument("--targets-steps", type=int, default=20)
-    ap.add_argument("--cpu-seqs", type=int, default=8,
+    ap.add_argument("--cpu-seqs", type=int, default=12,
                     help="sequences in the CPU oracle sample (0 disables it)")
     ap.add_argument("--dq", choices=("auto", "stored-p", "recompute"), default="auto",
                     help="dQ path of the backward: from stored P (needs ~2 bytes per (row, "
