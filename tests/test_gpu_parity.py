@@ -252,6 +252,25 @@ def test_dk_dv_bitwise_repeatable(hj):
             assert torch.equal(a, b)
 
 
+def test_stored_p_bitwise_repeatable(hj):
+    """The stored-P backward (P written by the key-owner pass, dQ from it)
+    gives the same bits on every replay, dQ included."""
+    ls = np.array([700, 300, 1000, 64])
+    H, D = 2, 128
+    off = wl.offsets_from_lengths(ls)
+    inp = make_inputs(ls, H, D, "bf16", 23)
+    off_t = torch.from_numpy(off).to(DEV)
+    ft = torch.from_numpy(wl.func_causal(ls, 5)).to(DEV)
+    ps = torch.empty(hj.pstore_bytes(off_t, H), dtype=torch.uint8, device=DEV)
+    args = (inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], off_t, ft, 0.09, 1000)
+    ref = hj.attn_bwd(*args, pstore=ps)
+    for _ in range(10):
+        ps.fill_(0xFF)  # stale bytes from an earlier call must not leak into dQ
+        g = hj.attn_bwd(*args, pstore=ps)
+        for a, b in zip(ref, g):
+            assert torch.equal(a, b)
+
+
 def test_check_inputs(hj):
     off = torch.tensor([0, 3, 7], dtype=torch.int64, device=DEV)
     hj.check_inputs(off, 7)
