@@ -200,7 +200,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}): "
-              "the operator has no cross-GPU step; see the sharding notes in DESIGN.md",
+              "the operator has no cross-GPU step; several GPUs each run their own slice of "
+              "the sequences",
               file=sys.stderr)
         return 2
 
