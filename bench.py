@@ -183,8 +183,8 @@ def cpu_baseline(cfg, t, off, nseq):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="hstu_2663", choices=wl.WORKLOADS)
     ap.add_argument("--targets-steps", type=int, default=20)
     ap.add_argument("--cpu-seqs", type=int, default=12,
