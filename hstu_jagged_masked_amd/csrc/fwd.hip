@@ -71,6 +71,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
   const int64_t rs = (int64_t)H * kD;  // row stride (elements)
   const int rs2 = H * kD * 2;          // row stride (bytes)
 
+  // the block's envelope first: the tile list, and with it the first copy,
+  // then need not wait behind the q and func loads
+  if (tid == 0) rows_envelope(P, u.rb, r0, kBM, L, ni, sEnv);
   // this lane's query row (B-operand column n of wave `wave`)
   const int row = r0 + wave * 32 + n;
   const bool row_ok = row < L;
@@ -89,7 +92,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
     if (j < ni && row_ok) row_interval(func, P.total, s + row, j, L, lo[j], hi[j]);
   }
 
-  if (tid == 0) rows_envelope(P, u.rb, r0, kBM, L, ni, sEnv);
   __syncthreads();
   int t_begin, t_end;
   envelope_tile_span(sEnv, ni, kBN, t_begin, t_end);
