@@ -122,6 +122,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   const int rs2 = H * kD * 2;
   const float c_exp = -alpha * kLog2e;
 
+  // the first window's step lists before the K / V row loads, so that they
+  // (and the first copy) do not wait behind them
+  const int nrb = (L + kRB - 1) / kRB;
+  const int4* env = P.env + (int64_t)u.rb * ni;
+  auto list_window = [&](int w0) {
+    if (wave == 0) {
+      int np, nf;
+      step_window(env, ni, L, nrb, w0, c0, c1, sPart, sFull, np, nf);
+      if (lane == 0) {
+        sCount[0] = np;
+        sCount[1] = nf;
+      }
+    }
+  };
+  list_window(0);
   // this lane's key column and its K / V rows (B operands: [k = d][n = key])
   const int col = c0 + wave * 32 + n;
   const bool col_ok = col < L;
@@ -293,17 +308,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     __syncthreads();
   };
 
-  const int nrb = (L + kRB - 1) / kRB;
-  const int4* env = P.env + (int64_t)u.rb * ni;
   for (int w0 = 0; w0 < nrb; w0 += kListWin) {
-    if (wave == 0) {
-      int np, nf;
-      step_window(env, ni, L, nrb, w0, c0, c1, sPart, sFull, np, nf);
-      if (lane == 0) {
-        sCount[0] = np;
-        sCount[1] = nf;
-      }
-    }
+    if (w0 > 0) list_window(w0);
     __syncthreads();
     const int n_part = sCount[0], n_full = sCount[1];
     walk(sPart, n_part, std::true_type{});
@@ -357,6 +363,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
   const int rs2 = H * kD * 2;
   const float c_exp = -alpha * kLog2e;
 
+  // the block's envelope first, so that the tile list does not wait behind
+  // the q, dO and func loads
+  if (tid == 0) rows_envelope(P, u.rb, r0, kQBM, L, ni, sEnv);
   const int row = r0 + wave * 32 + n;
   const bool row_ok = row < L;
   bf16x8 qf[kD / 16], gf[kD / 16];
@@ -376,7 +385,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
     hi[j] = 0;
     if (j < ni && row_ok) row_interval(func, P.total, s + row, j, L, lo[j], hi[j]);
   }
-  if (tid == 0) rows_envelope(P, u.rb, r0, kQBM, L, ni, sEnv);
   __syncthreads();
   int t_begin, t_end;
   envelope_tile_span(sEnv, ni, kQBN, t_begin, t_end);
