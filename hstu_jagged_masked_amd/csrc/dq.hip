@@ -75,20 +75,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
     return live;
   };
 
-  // key tiles the row blocks' union envelope spans
-  int kt_begin = INT32_MAX, kt_end = 0;  // (kt_begin >= 0 once set)
-  for (int rb = rb_a; rb <= (has_b ? rb_b : rb_a); ++rb) {
-#pragma unroll
-    for (int j = 0; j < kMaxNI; ++j) {
-      if (j < ni) {
-        const int4 e = env[(int64_t)rb * ni + j];
-        if (e.x < e.y) {
-          kt_begin = min(kt_begin, e.x / kKT);
-          kt_end = max(kt_end, (e.y - 1) / kKT + 1);
-        }
-      }
-    }
-  }
+  // every key tile of the sequence is a candidate: the window ballots below
+  // pick the live ones (one round of envelope reads instead of two)
+  const int kt_begin = 0, kt_end = (L + kKT - 1) / kKT;
   // Liveness of 64 key tiles at a time as ballot masks (bit j: tile w + j
   // reaches the first / second row block), so that the walk itself issues no
   // loads besides its copies and P loads.
