@@ -189,10 +189,10 @@ def main():
     ap.add_argument("--targets-steps", type=int, default=20)
     ap.add_argument("--cpu-seqs", type=int, default=12,
                     help="sequences in the CPU oracle sample (0 disables it)")
-    ap.add_argument("--dq", choices=("auto", "stored-p", "recompute"), default="auto",
+    ap.add_argument("--dq", choices=("stored-p", "recompute"), default="stored-p",
                     help="dQ path of the backward: from stored P (needs ~2 bytes per (row, "
-                         "column) pair of each sequence per head of HBM; 'auto' uses it when it "
-                         "fits) or recomputing the scores")
+                         "column) pair of each sequence per head of HBM) or recomputing the "
+                         "scores; the run fails rather than switch paths when memory is short")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="size of a plain device-to-device copy run once before timing; "
                          "counter runs scale HBM byte counters by it (0 disables it)")
@@ -230,8 +230,7 @@ def main():
         del src, dst
     pstore = None
     p_bytes = hj.pstore_bytes(t["off"], H)
-    free, _ = torch.cuda.mem_get_info(device)
-    use_p = args.dq == "stored-p" or (args.dq == "auto" and p_bytes + (16 << 30) < free)
+    use_p = args.dq == "stored-p"
     if use_p:
         pstore = torch.empty(p_bytes, dtype=torch.uint8, device=device)
     log(f"[bench] dQ path: {'stored P, %.1f GB' % (p_bytes / 1e9) if use_p else 'recompute'}")

@@ -60,7 +60,7 @@ def library() -> ctypes.CDLL:
     lib.hstu_max_nfunc.restype = i32
     lib.hstu_last_error.argtypes = []
     lib.hstu_last_error.restype = ctypes.c_char_p
-    lib.hstu_attn_workspace_size.argtypes = [i32, i32, i64, i64, i32, i32, i32, i32]
+    lib.hstu_attn_workspace_size.argtypes = [i32, i64, i64, i32, i32, i32, i32]
     lib.hstu_attn_workspace_size.restype = sz
     lib.hstu_attn_fwd.argtypes = [i32, P, P, P, P, P, i64, i64, i32, i32, P, i32, f32, i64, P, P,
                                   sz, P]
@@ -119,9 +119,9 @@ def max_nfunc() -> int:
     return library().hstu_max_nfunc()
 
 
-def workspace_size(is_bwd, dtype_code, B, total, H, D, nfunc, targets_only) -> int:
-    return int(library().hstu_attn_workspace_size(int(is_bwd), int(dtype_code), int(B), int(total),
-                                                  int(H), int(D), int(nfunc), int(targets_only)))
+def workspace_size(is_bwd, B, total, H, D, nfunc, targets_only) -> int:
+    return int(library().hstu_attn_workspace_size(int(is_bwd), int(B), int(total), int(H), int(D),
+                                                  int(nfunc), int(targets_only)))
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
@@ -157,7 +157,7 @@ def attn_fwd(q, k, v, seq_offsets, func, alpha, max_len, target_rows=None, out=N
             raise ValueError("q, k, v must be contiguous and share a dtype")
     code = _dtype_code(k)
     o = torch.empty_like(q) if out is None else out
-    ws_bytes = workspace_size(0, code, B, total, H, D, nfunc, target_rows is not None)
+    ws_bytes = workspace_size(0, B, total, H, D, nfunc, target_rows is not None)
     ws = _workspace(ws_bytes, k.device)
     _check(library().hstu_attn_fwd(
         code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_offsets), B, total, H, D, _ptr(func),
@@ -179,7 +179,8 @@ def pstore_bytes(seq_offsets, H) -> int:
 def attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None, pstore=None):
     """Backward.  With ``pstore`` (a CUDA uint8 tensor of at least
     ``pstore_bytes(seq_offsets, H)`` bytes; bf16, D = 128, full-length mode) the
-    stored-P path runs: no recomputation of the scores for dQ."""
+    stored-P path runs: no recomputation of the scores for dQ.  The size is
+    checked on the device: with a smaller buffer dq comes back as NaN."""
     B, total, H, D, nfunc = _common(q, k, seq_offsets, func, target_rows)
     for t in (q, k, v, dout):
         if not t.is_contiguous() or t.dtype != k.dtype:
@@ -188,7 +189,7 @@ def attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None,
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    ws_bytes = workspace_size(1, code, B, total, H, D, nfunc, target_rows is not None)
+    ws_bytes = workspace_size(1, B, total, H, D, nfunc, target_rows is not None)
     ws = _workspace(ws_bytes, k.device)
     if pstore is not None:
         if target_rows is not None or code != HSTU_BF16:
@@ -223,7 +224,7 @@ def visible_counts(seq_offsets, func, total=None, target_rows=None):
 def check_inputs(seq_offsets, total, target_rows=None):
     """Validate device-resident offsets / target rows (synchronizes)."""
     B = seq_offsets.numel() - 1
-    ws = _workspace(workspace_size(0, HSTU_BF16, B, total, 1, 128, 1, 0), seq_offsets.device)
+    ws = _workspace(workspace_size(0, B, total, 1, 128, 1, 0), seq_offsets.device)
     _check(library().hstu_attn_check_inputs(_ptr(seq_offsets), B, int(total), _ptr(target_rows),
                                             _ptr(ws), ws.numel(), _stream(seq_offsets.device)))
 

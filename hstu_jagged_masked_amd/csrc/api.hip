@@ -9,6 +9,7 @@
 
 #include "common.h"
 #include "hstu_attn.h"
+#include "pstore.h"
 
 namespace hstu {
 
@@ -40,10 +41,8 @@ bool mfma_path(int dtype, int D) { return dtype == HSTU_BF16 && D == 128; }
 
 }  // namespace
 
-bool plan_workspace(Plan& p, int is_bwd, int dtype, int64_t B, int64_t total, int H, int D,
-                    int nfunc, int targets_only) {
-  (void)dtype;
-  (void)D;
+bool plan_workspace(Plan& p, int is_bwd, int64_t B, int64_t total, int H, int D, int nfunc,
+                    int targets_only) {
   p = Plan();
   if (B < 1 || B > (1 << 24) || total < 0 || total > (int64_t)INT32_MAX || H < 1 || H > 255 ||
       nfunc < 1 || nfunc > kMaxNfunc)
@@ -129,7 +128,7 @@ int validate(Plan& plan, int is_bwd, int dtype, int64_t B, int64_t total, int H,
   if (!func && total > 0) return fail(HSTU_ERR_INVALID, "func is NULL");
   if (misaligned(seq_offsets) || misaligned(func) || misaligned(target_rows))
     return fail(HSTU_ERR_INVALID, "seq_offsets, func and target_rows must be 16-byte aligned");
-  if (!plan_workspace(plan, is_bwd, dtype, B, total, H, D, nfunc, target_rows != nullptr))
+  if (!plan_workspace(plan, is_bwd, B, total, H, D, nfunc, target_rows != nullptr))
     return fail(HSTU_ERR_UNSUPPORTED, "sizes out of range");
   if (workspace_bytes < plan.bytes || (!workspace && plan.bytes))
     return fail(HSTU_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
@@ -161,10 +160,10 @@ extern "C" int hstu_max_nfunc(void) { return kMaxNfunc; }
 
 extern "C" const char* hstu_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" size_t hstu_attn_workspace_size(int is_bwd, int dtype, int64_t B, int64_t total, int H,
-                                           int D, int nfunc, int targets_only) {
+extern "C" size_t hstu_attn_workspace_size(int is_bwd, int64_t B, int64_t total, int H, int D,
+                                           int nfunc, int targets_only) {
   Plan plan;
-  if (!plan_workspace(plan, is_bwd, dtype, B, total, H, D, nfunc, targets_only)) return 0;
+  if (!plan_workspace(plan, is_bwd, B, total, H, D, nfunc, targets_only)) return 0;
   return plan.bytes;
 }
 
@@ -247,7 +246,7 @@ extern "C" int hstu_attn_bwd(int dtype, const void* q, const void* k, const void
     if (e == hipSuccess) e = launch_units(P, Uq, 128, 1, H, kSlotQUnits, s);
     if (e != hipSuccess) return device_fail(e, "unit list");
     e = launch_mfma_bwd(q, k, v, dout, dq, dk, dv, P, Ukv, Uq, H, func, nfunc, alpha,
-                        inv_max_len, nullptr, s);
+                        inv_max_len, nullptr, 0, s);
   } else {
     e = launch_generic_bwd(dtype, D, q, k, v, dout, dq, dk, dv, P, H, func, nfunc, alpha,
                            inv_max_len, nullptr, s);
@@ -268,11 +267,10 @@ extern "C" size_t hstu_attn_pstore_bytes(const int64_t* seq_offsets, int64_t B, 
     int64_t x = seq_offsets[b] < 0 ? 0 : (seq_offsets[b] > total ? total : seq_offsets[b]);
     run = x > run ? x : run;
     const int64_t cur = b == B ? total : run;
-    const int64_t L = cur - prev;
-    blocks += cdiv64(L, 128) * cdiv64(L, 32);
+    blocks += pstore_seq_blocks(cur - prev);
     prev = cur;
   }
-  return (size_t)blocks * H * 8192;
+  return (size_t)blocks * H * kPBlockBytes;
 }
 
 extern "C" int hstu_attn_bwd_pstore(const void* q, const void* k, const void* v, const void* dout,
@@ -300,23 +298,17 @@ extern "C" int hstu_attn_bwd_pstore(const void* q, const void* k, const void* v,
   Prep P = prep_view(plan, workspace, (int)B, total);
   hipError_t e = launch_prep(P, seq_offsets, nullptr, func, nfunc, s);
   if (e != hipSuccess) return device_fail(e, "prep");
-  // the stored-P size follows from the device's sanitized lengths: read it
-  // back and refuse a buffer that is too small before any kernel writes P
-  int64_t blocks = 0;
-  e = hipMemcpyAsync(&blocks, P.pblk + B, sizeof(int64_t), hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) return device_fail(e, "reading the stored-P size");
-  const size_t need = (size_t)blocks * H * 8192;
-  if (pstore_bytes < need)
-    return fail(HSTU_ERR_WORKSPACE, "stored-P buffer of %zu bytes given, %zu needed", pstore_bytes,
-                need);
+  // The size the lengths need is known on the device only; the kernels
+  // compare it with pstore_bytes themselves (every P access is range-checked
+  // against the buffer, and dq is written as NaN when the buffer is too
+  // small), so nothing here waits for the device.
   Units Ukv = units_view(workspace, plan.off_units_b, plan.cap_b);
   Units Uq = units_view(workspace, plan.off_units_c, plan.cap_c);
   e = launch_units(P, Ukv, 128, 0, H, kSlotKvUnits, s);
   if (e == hipSuccess) e = launch_units(P, Uq, 128, 1, H, kSlotQUnits, s);
   if (e != hipSuccess) return device_fail(e, "unit list");
   e = launch_mfma_bwd(q, k, v, dout, dq, dk, dv, P, Ukv, Uq, H, func, nfunc, alpha, inv_max_len,
-                      static_cast<uint16_t*>(pstore), s);
+                      static_cast<uint16_t*>(pstore), (uint64_t)pstore_bytes, s);
   if (e != hipSuccess) return device_fail(e, "backward");
   return HSTU_OK;
 }
@@ -350,7 +342,7 @@ extern "C" int hstu_attn_check_inputs(const int64_t* seq_offsets, int64_t B, int
   if (misaligned(seq_offsets) || misaligned(target_rows))
     return fail(HSTU_ERR_INVALID, "seq_offsets and target_rows must be 16-byte aligned");
   Plan plan;
-  if (!plan_workspace(plan, 0, HSTU_BF16, B, total, 1, 128, 1, 0))
+  if (!plan_workspace(plan, 0, B, total, 1, 128, 1, 0))
     return fail(HSTU_ERR_UNSUPPORTED, "sizes out of range");
   if (workspace_bytes < plan.bytes || !workspace)
     return fail(HSTU_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,

@@ -32,6 +32,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "pstore.h"
 #include "tiles.h"
 
 namespace hstu {
@@ -83,9 +84,9 @@ __device__ __forceinline__ void step_window(const int4* env, int ni, int L, int 
 }
 
 // kStoreP: also store each half's P (bf16, as rounded for the dK product)
-// for the dQ pass.  Layout, per (sequence, head): blocks [128-key tile
-// kt][32-row half t] of 8 KiB, block (kt, t) at ((pblk[b] H + h nkt nsteps)
-// + kt nsteps + t) * 8 KiB with nsteps = ceil(L/32).  A block holds the
+// for the dQ pass, in the block layout of pstore.h (one 8 KiB block per
+// (128-key tile, 32-row half)), through a buffer resource over this key
+// tile's blocks clipped to the caller's buffer.  A block holds the
 // registers pb[hh] of the four waves as they are: [wave w][hh][lane (n, g)][8
 // bf16], i.e. key 32 w + n at row positions hh*16 + g*8 + 0..7, where row
 // position hh*16 + g*8 + e is query row (2 hh + e/4)*8 + g*4 + e%4 of the
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, Prep P, const int4* __restrict__ units, int H,
     const int32_t* __restrict__ func, int nfunc, float alpha, float out_scale,
-    uint16_t* __restrict__ pstore) {
+    uint16_t* __restrict__ pstore, uint64_t pstore_cap) {
   // two LDS stages as separate objects, so the compiler sees that the DMA
   // filling one stage does not alias the reads of the other
   __shared__ __attribute__((aligned(256))) uint16_t sQ0[kQStage], sQ1[kQStage];
@@ -159,18 +160,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
 
   const uint16_t* qh = q + s * rs + (int64_t)h * kD;
   const uint16_t* gh = dout + s * rs + (int64_t)h * kD;
-  // stored P: this workgroup's first block (uniform)
-  int64_t p_blk0 = 0;
-  if constexpr (kStoreP) {
-    const int64_t nkt = (L + kKvBN - 1) / kKvBN, nsteps = (L + kKvBM - 1) / kKvBM;
-    p_blk0 = u.pblk * H + h * nkt * nsteps + kt * nsteps;
-  }
+  // stored P: this workgroup's key tile's blocks, as a buffer resource
+  // clipped to the caller's buffer (stores past it are dropped)
+  const PRegion pr = kStoreP ? pstore_tile_region(u.pblk, H, h, L, kt, pstore_cap) : PRegion{0, 0};
+  const __amdgpu_buffer_rsrc_t p_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<char*>(pstore) + pr.base, (short)0, (int)pr.bytes, 0x00020000);
   // written once and read back by the dQ pass long after it has left L2:
   // non-temporal stores keep the Q / dO tiles cached instead
   auto p_store = [&](int r, const bf16x8* pv) {
-    uint16_t* blk = pstore + ((p_blk0 + r / kKvBM) << 12) + wave * 1024 + lane * 8;
-    __builtin_nontemporal_store(pv[0], reinterpret_cast<bf16x8*>(blk));
-    __builtin_nontemporal_store(pv[1], reinterpret_cast<bf16x8*>(blk + 512));
+    const int t = r / kKvBM;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const auto w = __builtin_bit_cast(
+          __attribute__((ext_vector_type(4))) unsigned int, pv[hf]);
+      __builtin_amdgcn_raw_buffer_store_b128(w, p_rsrc, (int)pstore_offset(t, 2 * wave + hf, lane),
+                                             0, kCacheNT);
+    }
   };
   // DMA of one 64-row step: wave w issues instructions I = w + 4i of each
   // tensor; lane l of instruction I fills LDS slot 64*I + l
@@ -549,7 +554,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
 hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const void* dout,
                            void* dq, void* dk, void* dv, const Prep& P, const Units& Ukv,
                            const Units& Uq, int H, const int32_t* func, int nfunc, float alpha,
-                           float inv_max_len, uint16_t* pstore, hipStream_t stream) {
+                           float inv_max_len, uint16_t* pstore, uint64_t pstore_cap,
+                           hipStream_t stream) {
   const float scale = alpha * inv_max_len;
   if (Ukv.cap > 0) {
     ProfScope ps(stream, pstore ? "k_bwd_kv_p" : "k_bwd_kv");
@@ -558,11 +564,11 @@ hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const vo
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout),
                        static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), P, Ukv.list, H,
-                       func, nfunc, alpha, scale, pstore);
+                       func, nfunc, alpha, scale, pstore, pstore_cap);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (pstore) return launch_dq_from_p(k, dq, P, Uq, H, nfunc, pstore, scale, stream);
+  if (pstore) return launch_dq_from_p(k, dq, P, Uq, H, nfunc, pstore, pstore_cap, scale, stream);
   if (Uq.cap > 0) {
     ProfScope ps(stream, "k_bwd_q");
     hipLaunchKernelGGL(k_bwd_q, dim3(Uq.cap), dim3(kThreads), 0, stream,

@@ -94,8 +94,8 @@ struct Plan {
 };
 
 // Fills `plan` for a call; returns false if sizes are out of range.
-bool plan_workspace(Plan& plan, int is_bwd, int dtype, int64_t B, int64_t total, int H, int D,
-                    int nfunc, int targets_only);
+bool plan_workspace(Plan& plan, int is_bwd, int64_t B, int64_t total, int H, int D, int nfunc,
+                    int targets_only);
 Prep prep_view(const Plan& plan, void* ws, int B, int64_t total);
 
 // ---------------------------------------------------------------------------
@@ -146,10 +146,11 @@ hipError_t launch_mfma_fwd(const void* q, const void* k, const void* v, void* o,
 hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const void* dout,
                            void* dq, void* dk, void* dv, const Prep& P, const Units& Ukv,
                            const Units& Uq, int H, const int32_t* func, int nfunc, float alpha,
-                           float inv_max_len, uint16_t* pstore, hipStream_t stream);
+                           float inv_max_len, uint16_t* pstore, uint64_t pstore_cap,
+                           hipStream_t stream);
 hipError_t launch_dq_from_p(const void* k, void* dq, const Prep& P, const Units& Uq, int H,
-                            int nfunc, const uint16_t* pstore, float out_scale,
-                            hipStream_t stream);
+                            int nfunc, const uint16_t* pstore, uint64_t pstore_cap,
+                            float out_scale, hipStream_t stream);
 
 // targets-only streaming kernels (any dtype, D); U lists 128-row key tiles
 int targets_chunk_rows();

@@ -12,7 +12,8 @@
 //     one of two stages, the next tile's copy in flight during this tile;
 //   * each wave's stored P block (8 KiB, the key-owner kernel's registers as
 //     they were: key-major, 8 row positions per 16 bytes) -> registers by
-//     plain 16-byte loads, two tiles ahead;
+//     16-byte buffer loads (range-checked against the key tile's blocks and
+//     the caller's buffer), two tiles ahead;
 //   * P transposed through a wave-private LDS buffer, 32 keys at a time, into
 //     the B operand of dQ^T += K^T P^T (row position per lane, 8 keys);
 //   * dQ^T += K^T P^T on MFMA, A = K^T by LDS transpose reads.
@@ -22,6 +23,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "pstore.h"
 #include "tiles.h"
 
 namespace hstu {
@@ -43,7 +45,7 @@ using S1 = std::integral_constant<int, 1>;
 __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
     const uint16_t* __restrict__ k, uint16_t* __restrict__ dq, Prep P,
     const int4* __restrict__ units, int H, int nfunc, const uint16_t* __restrict__ pstore,
-    float out_scale) {
+    uint64_t pstore_cap, float out_scale) {
   __shared__ __attribute__((aligned(256))) uint16_t sK0[kKStage], sK1[kKStage];
   // per wave: P of 32 keys as [key][32 row positions], 64-byte rows, 16-byte
   // chunk c of key row r at position c ^ ((r / 4) mod 4)
@@ -64,6 +66,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
   // this wave's step and the row block whose envelope decides its tiles
   const int q0 = r0 + wave * kStep;
   const bool wave_rows = q0 < L;
+
+  // a stored-P buffer smaller than these lengths need held no complete P:
+  // the rows get NaN, so that the failure cannot pass unseen
+  if ((uint64_t)P.pblk[P.B] * (uint64_t)H * kPBlockBytes > pstore_cap) {
+    const int row = r0 + wave * 32 + n;
+    if (row < L) {
+      uint16_t* op = dq + (s + row) * rs + (int64_t)h * kD + g * 64;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint4*>(op + j * 8) = make_uint4(0x7fc07fc0u, 0x7fc07fc0u,
+                                                           0x7fc07fc0u, 0x7fc07fc0u);
+    }
+    return;
+  }
   const int nrb = (L + kRB - 1) / kRB;
   const int4* env = P.env + (int64_t)u.rb * ni;
   const int rb_a = r0 / kRB, rb_b = rb_a + 1;  // the workgroup's two row blocks
@@ -112,9 +128,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
     return -1;
   };
 
-  const int64_t nkt = (L + kKT - 1) / kKT, nsteps = (L + kStep - 1) / kStep;
-  // this wave's stored-P blocks: the kt-th at pw + kt * nsteps * 4096 elements
-  const uint16_t* pw = pstore + ((u.pblk * H + h * nkt * nsteps + q0 / kStep) << 12) + lane * 8;
   const uint16_t* kh = k + s * rs + (int64_t)h * kD;
 
   int kdoff[kKDma];
@@ -130,12 +143,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
       lds_dma16_raw(rk, (st ? sK1 : sK0) + (wave + 4 * i) * 512, kdoff[i]);
   };
   // P is read exactly once: non-temporal loads, so that it does not push the
-  // K tiles (re-read by every query block of the sequence) out of L2
+  // K tiles (re-read by every query block of the sequence) out of L2.  The
+  // loads go through a resource over key tile kt's blocks (clipped to the
+  // caller's buffer): a wave whose step lies past the sequence end reads
+  // zeros there instead of another tile's blocks or memory past the buffer.
   auto load_p = [&](int kt, bf16x8* dst) {
-    const uint16_t* src = pw + (((int64_t)kt * nsteps) << 12);
+    const PRegion pr = pstore_tile_region(u.pblk, H, h, L, kt, pstore_cap);
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(pstore)) + pr.base, (short)0,
+        (int)pr.bytes, 0x00020000);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      dst[ks] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(src + ks * 512));
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(
+          rp, (int)pstore_offset(q0 / kStep, ks, lane), 0, kCacheNT);
+      dst[ks] = __builtin_bit_cast(bf16x8, w);
+    }
   };
 
   // K^T transpose reads: lane j of 16-lane group G takes key rows 8*(G/2) + j/4
@@ -280,13 +302,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dq(
 }  // namespace
 
 hipError_t launch_dq_from_p(const void* k, void* dq, const Prep& P, const Units& Uq, int H,
-                            int nfunc, const uint16_t* pstore, float out_scale,
-                            hipStream_t stream) {
+                            int nfunc, const uint16_t* pstore, uint64_t pstore_cap,
+                            float out_scale, hipStream_t stream) {
   if (Uq.cap == 0) return hipSuccess;
   ProfScope ps(stream, "k_bwd_dq");
   hipLaunchKernelGGL(k_bwd_dq, dim3(Uq.cap), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(k), static_cast<uint16_t*>(dq), P, Uq.list, H,
-                     nfunc, pstore, out_scale);
+                     nfunc, pstore, pstore_cap, out_scale);
   return hipGetLastError();
 }
 

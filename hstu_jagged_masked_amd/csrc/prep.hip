@@ -6,6 +6,7 @@
 // interval 0 = [0, f0), interval j = [f(2j-1), f(2j)), empty when end <= start,
 // visible set = union, bounds sequence-local and clipped to [0, L).
 #include "common.h"
+#include "pstore.h"
 
 namespace hstu {
 
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prep P, const int64_t* __
       int64_t nblk = 0;
       if (b < B) {
         const int L = (int)(P.so[b + 1] - P.so[b]);
-        nblk = (int64_t)cdiv(L, 128) * cdiv(L, 32);
+        nblk = pstore_seq_blocks(L);
       }
       int64_t t_blk;
       const int64_t i_blk = block_inclusive_scan(nblk, scan64, &t_blk, SumOp());

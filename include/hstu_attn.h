@@ -85,11 +85,12 @@ int hstu_max_nfunc(void);
 const char* hstu_last_error(void);
 
 /* Bytes of device workspace a call needs (fwd: is_bwd = 0, bwd: 1) for these
- * sizes; targets_only != 0 for the targets-only mode.  Returns 0 for sizes the
- * library does not support (the entry point then reports why).  The workspace
- * is scratch: its contents need not be preserved between calls. */
-size_t hstu_attn_workspace_size(int is_bwd, int dtype, int64_t B, int64_t total, int H, int D,
-                                int nfunc, int targets_only);
+ * sizes (either dtype); targets_only != 0 for the targets-only mode.  Returns
+ * 0 for sizes the library does not support (the entry point then reports
+ * why).  The workspace is scratch: its contents need not be preserved between
+ * calls. */
+size_t hstu_attn_workspace_size(int is_bwd, int64_t B, int64_t total, int H, int D, int nfunc,
+                                int targets_only);
 
 /* Forward: writes o ([total,H,D], or [B,H,D] when target_rows != NULL).
  * q has the shape of o; k, v are [total,H,D]. */
@@ -116,11 +117,15 @@ int hstu_attn_bwd(int dtype, const void* q, const void* k, const void* v, const 
  * from them.  This trades HBM capacity and bandwidth (about 2 bytes per
  * (row, column) pair of each sequence's L x L square, per head) for 4*D of
  * the 14*D executed flops per visible pair.
- * pstore: device buffer, 256-byte aligned, of at least hstu_attn_pstore_bytes
- * bytes; scratch (contents not preserved).  The call reads the needed size
- * back from the device (it synchronizes `stream`, so it cannot be captured in
- * a HIP graph) and returns HSTU_ERR_WORKSPACE, enqueueing nothing more, when
- * pstore_bytes is smaller.  dk, dv and dq are deterministic. */
+ * pstore: device buffer, 256-byte aligned, of pstore_bytes bytes; scratch
+ * (contents not preserved).  It must hold hstu_attn_pstore_bytes bytes for
+ * the device offsets.  Those are known on the device only, so the call does
+ * not wait for them: every access to pstore is range-checked against
+ * pstore_bytes (nothing outside the buffer is read or written, whatever its
+ * size), and if the buffer is smaller than the offsets need, dk and dv are
+ * still correct and every row of dq is written as NaN.  The call enqueues
+ * its work and returns without synchronizing `stream`.  dk, dv and dq are
+ * deterministic. */
 int hstu_attn_bwd_pstore(const void* q, const void* k, const void* v, const void* dout, void* dq,
                          void* dk, void* dv, const int64_t* seq_offsets, int64_t B, int64_t total,
                          int H, int D, const int32_t* func, int nfunc, float alpha,

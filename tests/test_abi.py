@@ -54,12 +54,12 @@ def test_max_nfunc(lib):
 
 def test_workspace_size(lib):
     ws = lib.hstu_attn_workspace_size
-    assert ws(0, 0, 32, 32 * 1024, 4, 128, 5, 0) > 0
-    assert ws(1, 0, 32, 32 * 1024, 4, 128, 5, 0) >= ws(0, 0, 32, 32 * 1024, 4, 128, 5, 0)
-    assert ws(0, 0, 32, 32 * 1024, 4, 128, 5, 1) > ws(0, 0, 32, 32 * 1024, 4, 128, 5, 0)
-    assert ws(0, 0, 0, 10, 4, 128, 5, 0) == 0      # B < 1
-    assert ws(0, 0, 2, 10, 4, 128, 11, 0) == 0     # nfunc too large
-    assert ws(0, 0, 2, -1, 4, 128, 5, 0) == 0      # negative total
+    assert ws(0, 32, 32 * 1024, 4, 128, 5, 0) > 0
+    assert ws(1, 32, 32 * 1024, 4, 128, 5, 0) >= ws(0, 32, 32 * 1024, 4, 128, 5, 0)
+    assert ws(0, 32, 32 * 1024, 4, 128, 5, 1) > ws(0, 32, 32 * 1024, 4, 128, 5, 0)
+    assert ws(0, 0, 10, 4, 128, 5, 0) == 0      # B < 1
+    assert ws(0, 2, 10, 4, 128, 11, 0) == 0     # nfunc too large
+    assert ws(0, 2, -1, 4, 128, 5, 0) == 0      # negative total
 
 
 FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation
