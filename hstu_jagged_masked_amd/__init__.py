@@ -9,6 +9,7 @@ library is missing the import of the op raises.
 Entry points mirror the C ABI (include/hstu_attn.h):
 
     attn_fwd(q, k, v, seq_offsets, func, alpha, max_len, target_rows=None) -> o
+    attn_fwd_noalloc(...)  # the same without a workspace (fixed per-device array)
     attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None,
              pstore=None) -> dq, dk, dv
     pstore_bytes(seq_offsets, H) -> bytes of the stored-P buffer attn_bwd(pstore=...) needs
@@ -65,6 +66,9 @@ def library() -> ctypes.CDLL:
     lib.hstu_attn_fwd.argtypes = [i32, P, P, P, P, P, i64, i64, i32, i32, P, i32, f32, i64, P, P,
                                   sz, P]
     lib.hstu_attn_fwd.restype = i32
+    lib.hstu_attn_fwd_noalloc.argtypes = [i32, P, P, P, P, P, i64, i64, i32, i32, P, i32, f32,
+                                          i64, P, P]
+    lib.hstu_attn_fwd_noalloc.restype = i32
     lib.hstu_attn_bwd.argtypes = [i32, P, P, P, P, P, P, P, P, i64, i64, i32, i32, P, i32, f32,
                                   i64, P, P, sz, P]
     lib.hstu_attn_bwd.restype = i32
@@ -88,7 +92,7 @@ def library() -> ctypes.CDLL:
 
 
 EXPORTED = ("hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size", "hstu_attn_fwd",
-            "hstu_attn_bwd", "hstu_attn_bwd_pstore", "hstu_attn_pstore_bytes",
+            "hstu_attn_fwd_noalloc", "hstu_attn_bwd", "hstu_attn_bwd_pstore", "hstu_attn_pstore_bytes",
             "hstu_attn_visible_counts", "hstu_attn_check_inputs",
             "hstu_profile_enable", "hstu_profile_read", "hstu_profile_reset")
 
@@ -163,6 +167,22 @@ def attn_fwd(q, k, v, seq_offsets, func, alpha, max_len, target_rows=None, out=N
         code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_offsets), B, total, H, D, _ptr(func),
         nfunc, float(alpha), int(max_len), _ptr(target_rows), _ptr(ws), ws.numel(),
         _stream(k.device)))
+    return o
+
+
+def attn_fwd_noalloc(q, k, v, seq_offsets, func, alpha, max_len, target_rows=None, out=None):
+    """attn_fwd through the entry point that takes no workspace (the library's
+    fixed per-device array serves instead; larger sizes raise).  ``out`` lets a
+    caller that cannot allocate pass the output buffer too."""
+    B, total, H, D, nfunc = _common(q, k, seq_offsets, func, target_rows)
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype != k.dtype:
+            raise ValueError("q, k, v must be contiguous and share a dtype")
+    code = _dtype_code(k)
+    o = torch.empty_like(q) if out is None else out
+    _check(library().hstu_attn_fwd_noalloc(
+        code, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(seq_offsets), B, total, H, D, _ptr(func),
+        nfunc, float(alpha), int(max_len), _ptr(target_rows), _stream(k.device)))
     return o
 
 

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -206,6 +207,78 @@ extern "C" int hstu_attn_fwd(int dtype, const void* q, const void* k, const void
   }
   if (e != hipSuccess) return device_fail(e, "forward");
   return HSTU_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The forward without a caller workspace, for callers that cannot allocate
+// device memory.  Its workspace is `scratch`, a fixed array in device memory
+// that every GPU the library runs on holds (one copy per device) until the
+// process ends.  Host code never passes the array's name to a kernel or a
+// copy: the name is a host-side stand-in.  It uses the device address that
+// hipGetSymbolAddress returns, fetched once per device with that device
+// current and kept in g_scratch_ptr.  Every kernel of the forward writes the
+// workspace bytes it later reads (the previous call's contents are never
+// used), so nothing is cleared between calls.  Calls that overlap on one
+// device share the array and race.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The scratch array's device address on the device of `stream` (the current
+// device for the null stream).
+int scratch_address(hipStream_t stream, void** out) {
+  int cur = -1, dev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return device_fail(e, "hipStreamGetDevice");
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HSTU_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return device_fail(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return device_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(HSTU_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" int hstu_attn_fwd_noalloc(int dtype, const void* q, const void* k, const void* v,
+                                     void* o, const int64_t* seq_offsets, int64_t B,
+                                     int64_t total, int H, int D, const int32_t* func, int nfunc,
+                                     float alpha, int64_t max_len, const int32_t* target_rows,
+                                     void* stream) {
+  Plan plan;
+  if (plan_workspace(plan, 0, B, total, H, D, nfunc, target_rows != nullptr) &&
+      plan.bytes > kScratchBytes)
+    return fail(HSTU_ERR_UNSUPPORTED,
+                "these sizes need %zu bytes of workspace; the no-allocation forward holds %zu "
+                "(use hstu_attn_fwd with a workspace)",
+                plan.bytes, kScratchBytes);
+  void* ws = nullptr;
+  int st = scratch_address(static_cast<hipStream_t>(stream), &ws);
+  if (st) return st;
+  return hstu_attn_fwd(dtype, q, k, v, o, seq_offsets, B, total, H, D, func, nfunc, alpha,
+                       max_len, target_rows, ws, kScratchBytes, stream);
 }
 
 extern "C" int hstu_attn_bwd(int dtype, const void* q, const void* k, const void* v,

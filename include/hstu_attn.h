@@ -100,6 +100,22 @@ int hstu_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* 
                   const int32_t* target_rows, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/* The forward of hstu_attn_fwd (same arguments, same kernels, same results)
+ * without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Its workspace is a fixed 32 MiB array in device memory
+ * that the library holds on every GPU it runs on until the process ends; the
+ * call itself allocates nothing.  Sizes whose workspace
+ * (hstu_attn_workspace_size) exceeds 32 MiB are rejected with
+ * HSTU_ERR_UNSUPPORTED before anything is enqueued; full-length calls up to
+ * about 8 million tokens at H = 4 fit.  The array is shared by every call on
+ * a GPU: calls that overlap on one GPU (other streams, other threads) race
+ * and must not be issued. */
+int hstu_attn_fwd_noalloc(int dtype, const void* q, const void* k, const void* v, void* o,
+                          const int64_t* seq_offsets, int64_t B, int64_t total, int H, int D,
+                          const int32_t* func, int nfunc, float alpha, int64_t max_len,
+                          const int32_t* target_rows, void* stream);
+
 /* Backward: from dout (shape of o) writes dq (shape of q) and dk, dv
  * ([total,H,D]).  dk and dv are deterministic (bitwise repeatable); so is dq. */
 int hstu_attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* dout,

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size",
-                            "hstu_attn_fwd", "hstu_attn_bwd", "hstu_attn_bwd_pstore",
+                            "hstu_attn_fwd", "hstu_attn_fwd_noalloc", "hstu_attn_bwd",
+                            "hstu_attn_bwd_pstore",
                             "hstu_attn_pstore_bytes", "hstu_attn_visible_counts",
                             "hstu_attn_check_inputs", "hstu_profile_enable",
                             "hstu_profile_read", "hstu_profile_reset"])
@@ -159,3 +160,14 @@ def test_bwd_pstore_rejects_bad_arguments(lib):
     assert call(pstore=None) == -1 and "pstore is NULL" in lib.hstu_last_error().decode()
     assert call(pstore=P(FAKE + 16)) == -1 and "256-byte" in lib.hstu_last_error().decode()
     assert call(ws_bytes=16) == -3
+
+
+def test_fwd_noalloc_rejects_sizes_beyond_its_array(lib):
+    """Sizes whose workspace exceeds the fixed array are refused on the host
+    before any device call (the library never touches the fake pointers)."""
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    B, total = 1 << 20, 1 << 30  # workspace far beyond 32 MiB
+    assert lib.hstu_attn_workspace_size(0, B, total, 4, 128, 5, 0) > 32 << 20
+    st = lib.hstu_attn_fwd_noalloc(0, f, f, f, f, f, B, total, 4, 128, f, 5, 0.1, 8, None, None)
+    assert st == -2 and "no-allocation forward holds 33554432" in lib.hstu_last_error().decode()
