@@ -2,8 +2,11 @@
 launch configuration bench.py times.
 
 Every output of a sequence (O, dQ, dK, dV of its rows) depends only on that
-sequence's rows, so the oracle run on a few whole sequences gives exact
-expected values for them; the small SLA workloads are checked in full.
+sequence's rows, so the oracle run on 32 whole sequences gives exact expected
+values for them (the longest, the shortest, the median and the rest spread
+over the batch); the small SLA workloads are checked in full, and the
+targets-only mode on every candidate.  Both backward paths (recompute and
+stored P) are checked on every shape whose timing is reported.
 Visible counts are checked for every row against closed forms where the
 mask has one, else against the oracle on the sampled sequences.
 """
@@ -67,23 +70,35 @@ def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False, pstore=False)
     """fwd+bwd on the whole workload; oracle on the sequences `seqs`.  With
     `repeat`, a second fwd+bwd must reproduce every output bit for bit (each
     output element is written by one workgroup in a fixed order, so any
-    difference is a race)."""
+    difference is a race).  With `pstore`, the stored-P backward runs too (after
+    the default one, on the same inputs) and is checked against the same
+    oracle values, and its dk, dv must equal the default path's bit for bit."""
     t, off = device_inputs(cfg)
     func = torch.from_numpy(func_np).to(DEV)
-    ps = None
-    if pstore:
-        ps = torch.empty(hj.pstore_bytes(t["off"], cfg["H"]), dtype=torch.uint8, device=DEV)
     o = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], func, cfg["alpha"], cfg["max_len"])
     dq, dk, dv = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
-                             cfg["max_len"], pstore=ps)
+                             cfg["max_len"])
     if repeat:
         o2 = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], func, cfg["alpha"], cfg["max_len"])
         g2 = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
-                         cfg["max_len"], pstore=ps)
+                         cfg["max_len"])
         for nm, a, b in zip(("o", "dq", "dk", "dv"), (o, dq, dk, dv), (o2,) + tuple(g2)):
             assert torch.equal(a, b), f"{cfg['name']}.{nm}: second run differs"
         del o2, g2
-    del ps
+    gp = None
+    if pstore:
+        ps = torch.empty(hj.pstore_bytes(t["off"], cfg["H"]), dtype=torch.uint8, device=DEV)
+        gp = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
+                         cfg["max_len"], pstore=ps)
+        if repeat:
+            ps.fill_(0xFF)  # stale bytes must not reach dq
+            gp2 = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
+                              cfg["max_len"], pstore=ps)
+            for nm, a, b in zip(("dq", "dk", "dv"), gp, gp2):
+                assert torch.equal(a, b), f"{cfg['name']}.pstore.{nm}: second run differs"
+            del gp2
+        del ps
+        assert torch.equal(gp[1], dk) and torch.equal(gp[2], dv), "stored-P dk/dv differ"
     torch.cuda.synchronize()
     rows, sub_off = oracle.subset(off, seqs)
     rows_t = torch.from_numpy(rows).to(DEV)
@@ -94,14 +109,21 @@ def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False, pstore=False)
     want = oracle.bwd(q, k, v, do, sub_off, f_sub, cfg["alpha"], cfg["max_len"])
     for nm, got, w in zip(("o", "dq", "dk", "dv"), (o, dq, dk, dv), (want_o,) + want):
         check(f"{cfg['name']}{nfunc_label}.{nm}", got.index_select(0, rows_t), w)
+    if gp is not None:
+        check(f"{cfg['name']}{nfunc_label}.pstore.dq", gp[0].index_select(0, rows_t), want[0])
     return (o, dq, dk, dv), t, off
 
 
-def sample_seqs(lengths, n_extra=1):
+def sample_seqs(lengths, n=32):
+    """n sequences: the longest, the shortest, the median, the rest spread
+    evenly over the batch."""
     order = np.argsort(lengths, kind="stable")
-    picks = [int(order[-1]), int(order[0]), int(order[len(order) // 2])]
-    picks += [int(i) for i in np.linspace(0, len(lengths) - 1, n_extra + 2)[1:-1]]
-    return sorted(set(picks))
+    picks = {int(order[-1]), int(order[0]), int(order[len(order) // 2])}
+    for i in np.linspace(0, len(lengths) - 1, n):
+        if len(picks) >= n:
+            break
+        picks.add(int(i))
+    return sorted(picks)
 
 
 def test_sla_1k_full(hj):
@@ -132,22 +154,18 @@ def test_sla_2k_full_and_nfunc3_bitwise(hj):
 
 @pytest.mark.parametrize("name", ["hstu_2663", "hstu_ragged", "hstu_4086"])
 def test_hstu_layer_shapes_sampled(hj, name):
+    """The production layer shapes: both backward paths (recompute and stored
+    P, whose buffer is 59 / 60 / 137 GB here), 32 sequences against the
+    oracle, every output repeated bit for bit, exact causal counts."""
     cfg = wl.workload(name)
     ls = cfg["lengths"]
     f = cfg["func"](ls, 5)
-    run_full(hj, cfg, f, sample_seqs(ls), repeat=True)
+    run_full(hj, cfg, f, sample_seqs(ls), repeat=True, pstore=True)
     off_t = torch.from_numpy(wl.offsets_from_lengths(ls)).to(DEV)
     counts, tot = hj.visible_counts(off_t, torch.from_numpy(f).to(DEV), int(ls.sum()))
     assert np.array_equal(counts.cpu().numpy(), wl.local_rows(ls) + 1), "causal counts"
     assert int(tot.item()) == int(np.sum(ls * (ls + 1) // 2))
-
-
-def test_hstu_2663_pstore_sampled(hj):
-    """The stored-P backward at the benchmark shape (a 58 GB P buffer)."""
-    cfg = wl.workload("hstu_2663")
-    ls = cfg["lengths"]
-    run_full(hj, cfg, cfg["func"](ls, 5), sample_seqs(ls), nfunc_label=".pstore", repeat=True,
-             pstore=True)
+    torch.cuda.empty_cache()
 
 
 def test_three_interval_sampled(hj):
@@ -155,7 +173,7 @@ def test_three_interval_sampled(hj):
     ls = cfg["lengths"]
     f = cfg["func"](ls, 5)
     seqs = sample_seqs(ls)
-    run_full(hj, cfg, f, seqs)
+    run_full(hj, cfg, f, seqs, pstore=True)
     off = wl.offsets_from_lengths(ls)
     off_t = torch.from_numpy(off).to(DEV)
     counts, _ = hj.visible_counts(off_t, torch.from_numpy(f).to(DEV), int(off[-1]))
@@ -165,13 +183,12 @@ def test_three_interval_sampled(hj):
     assert np.array_equal(counts[rows], want)
 
 
-@pytest.mark.parametrize("pstore", [False, True])
-def test_onerank_sampled(hj, pstore):
+def test_onerank_sampled(hj):
     cfg = wl.workload("onerank")
     ls = cfg["lengths"]
     f = cfg["func"](ls, 5)
     seqs = sample_seqs(ls)
-    run_full(hj, cfg, f, seqs, nfunc_label=".pstore" if pstore else "", pstore=pstore)
+    run_full(hj, cfg, f, seqs, pstore=True)
     off = wl.offsets_from_lengths(ls)
     off_t = torch.from_numpy(off).to(DEV)
     counts, tot = hj.visible_counts(off_t, torch.from_numpy(f).to(DEV), int(off[-1]))
@@ -180,9 +197,10 @@ def test_onerank_sampled(hj, pstore):
     assert int(tot.item()) == want
 
 
-def test_hstu_2663_targets_only_sampled(hj):
-    """Targets-only at the production shape: candidates of 64 sampled
-    sequences checked (o, dq for the candidates; dk, dv for all their rows)."""
+def test_hstu_2663_targets_only_all_candidates(hj):
+    """Targets-only at the production shape: o and dq of all 1024 candidates
+    and dk, dv of every row of every sequence against the oracle (in chunks
+    of 128 sequences)."""
     cfg = wl.workload("hstu_2663")
     ls = cfg["lengths"]
     f_np = cfg["func"](ls, 5)
@@ -194,22 +212,25 @@ def test_hstu_2663_targets_only_sampled(hj):
     dq, dk, dv = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
                              cfg["max_len"], tr)
     torch.cuda.synchronize()
-    seqs = list(range(0, len(ls), 16))
-    rows, sub_off = oracle.subset(off, seqs)
-    rows_t = torch.from_numpy(rows).to(DEV)
-    seq_t = torch.tensor(seqs, device=DEV)
-    k = to64(t["k"].index_select(0, rows_t))
-    v = to64(t["v"].index_select(0, rows_t))
-    q = to64(t["q"].index_select(0, seq_t))
-    do = to64(t["do"].index_select(0, seq_t))
-    f_sub = np.ascontiguousarray(f_np[:, rows])
-    tr_sub = tr_np[seqs]
-    want_o = oracle.fwd(q, k, v, sub_off, f_sub, cfg["alpha"], cfg["max_len"], tr_sub)
-    wq, wk, wv = oracle.bwd(q, k, v, do, sub_off, f_sub, cfg["alpha"], cfg["max_len"], tr_sub)
-    check("targets.o", o.index_select(0, seq_t), want_o)
-    check("targets.dq", dq.index_select(0, seq_t), wq)
-    check("targets.dk", dk.index_select(0, rows_t), wk)
-    check("targets.dv", dv.index_select(0, rows_t), wv)
+    for c0 in range(0, len(ls), 128):
+        seqs = list(range(c0, min(c0 + 128, len(ls))))
+        rows, sub_off = oracle.subset(off, seqs)
+        rows_t = torch.from_numpy(rows).to(DEV)
+        seq_t = torch.tensor(seqs, device=DEV)
+        k = to64(t["k"].index_select(0, rows_t))
+        v = to64(t["v"].index_select(0, rows_t))
+        q = to64(t["q"].index_select(0, seq_t))
+        do = to64(t["do"].index_select(0, seq_t))
+        f_sub = np.ascontiguousarray(f_np[:, rows])
+        tr_sub = tr_np[seqs]
+        want_o = oracle.fwd(q, k, v, sub_off, f_sub, cfg["alpha"], cfg["max_len"], tr_sub)
+        wq, wk, wv = oracle.bwd(q, k, v, do, sub_off, f_sub, cfg["alpha"], cfg["max_len"],
+                                tr_sub)
+        for nm, got, want in (("o", o.index_select(0, seq_t), want_o),
+                              ("dq", dq.index_select(0, seq_t), wq),
+                              ("dk", dk.index_select(0, rows_t), wk),
+                              ("dv", dv.index_select(0, rows_t), wv)):
+            check(f"targets[{c0}:{c0 + len(seqs)}].{nm}", got, want)
     counts, tot = hj.visible_counts(t["off"], func, int(off[-1]), tr)
     assert np.array_equal(counts.cpu().numpy(), ls.astype(np.int32))
     assert int(tot.item()) == int(ls.sum())
