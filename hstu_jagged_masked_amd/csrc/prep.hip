@@ -189,35 +189,151 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prep P, const int64_t* __
   }
 }
 
-// Unit list for tiles of `tile` rows, one record per workgroup.  Unit lam
-// (in list order: sequence p of the dealt order owns [H*T[p], H*T[p+1]);
-// within it head-major, tiles in decreasing index when `descending`, heaviest
-// first for prefix-like masks, else increasing) runs on the workgroup that
-// xcd_slot maps to lam, so each XCD takes a contiguous share of the list.
-__global__ void k_units(Prep P, Units U, int tile, int descending, int H, int count_slot) {
-  const int bid = blockIdx.x * blockDim.x + threadIdx.x;
+constexpr int kUnitThreads = 1024;
+// Lists of at most this many units run in a few rounds of the GPU's
+// workgroup slots: their critical path is the heaviest unit, so they are
+// ordered heaviest first instead of sequence by sequence.
+constexpr int kSmallUnits = 4096;
+constexpr int kUnitsPerThread = kSmallUnits / kUnitThreads;
+
+// Unit lam of the sequence-major order: sequence p of the dealt order owns
+// [H*T[p], H*T[p+1]); within it head-major, position tr in the sequence's
+// tile order (decreasing tile index when `descending`, else increasing).
+struct UnitPos {
+  int p, nt, h, tr;
+};
+
+__device__ __forceinline__ UnitPos unit_pos(const int* T, int B, int H, int lam) {
+  UnitPos u;
+  u.p = upper_index(T, B, lam / H);
+  u.nt = T[u.p + 1] - T[u.p];
+  const int r = lam - H * T[u.p];
+  u.h = r / u.nt;
+  u.tr = r - u.h * u.nt;
+  return u;
+}
+
+// The two int4 of a unit's record.
+struct UnitRecord {
+  int4 a, c;
+};
+
+__device__ __forceinline__ UnitRecord unit_record(const Prep& P, const UnitPos& u,
+                                                  int descending) {
+  const int b = P.order[u.p];
+  const int64_t s = P.so[b];
+  const int64_t pb = P.pblk ? P.pblk[b] : 0;
+  UnitRecord r;
+  r.a = make_int4(b, descending ? u.nt - 1 - u.tr : u.tr, u.h, (int)(P.so[b + 1] - s));
+  r.c = make_int4((int)s, P.rb_off[b], (int)(uint32_t)(uint64_t)pb,
+                  (int)(uint32_t)((uint64_t)pb >> 32));
+  return r;
+}
+
+__device__ __forceinline__ void put_record(int4* list, int64_t at, int4 a, int4 c) {
+  list[2 * at] = a;
+  list[2 * at + 1] = c;
+}
+
+// Unit list for tiles of `tile` rows, one record per workgroup.
+// Long lists (more than kSmallUnits units): unit lam of the sequence-major
+// order runs on the workgroup that xcd_slot maps to lam, so each XCD takes a
+// contiguous share of the list and a sequence's tiles, which re-read the same
+// rows, share an L2; sequences come longest first and, within one, tiles
+// heaviest first for prefix-like masks.
+// Short lists: workgroup 0 sorts the units by a work estimate, heaviest
+// first -- for query tiles (`descending`) the higher tile index, for key tiles
+// the more tiles from it to the end of its sequence, which is what a causal
+// or prefix mask makes them cost -- and unit i runs on workgroup i, so the
+// heavy units start in the first round, spread over the XCDs.  (Units of
+// equal estimate take positions in an order the atomics decide; every unit
+// computes the same outputs wherever it runs.)
+__global__ __launch_bounds__(kUnitThreads) void k_units(Prep P, Units U, int tile,
+                                                        int descending, int H,
+                                                        int count_slot) {
+  __shared__ int hist[kSmallUnits];
+  __shared__ int part[kUnitThreads / 64];
+  __shared__ int smax;
+  const int tid = threadIdx.x;
+  const int bid = blockIdx.x * blockDim.x + tid;
   const int* T = tile == 64 ? P.tiles64 : P.tiles128;
   const int B = P.B;
   const int n = H * T[B];
   if (bid == 0) P.flags[count_slot] = n;
-  if (bid >= U.cap) return;
-  const int lam = xcd_slot(bid, n);
-  int4* rec = U.list + 2 * (int64_t)bid;
-  if (lam < 0) {
-    rec[0] = make_int4(-1, 0, 0, 0);
-    rec[1] = make_int4(0, 0, 0, 0);
+  const int4 idle_a = make_int4(-1, 0, 0, 0), idle_c = make_int4(0, 0, 0, 0);
+  if (n > kSmallUnits) {
+    if (bid >= U.cap) return;
+    const int lam = xcd_slot(bid, n);
+    if (lam < 0) {
+      put_record(U.list, bid, idle_a, idle_c);
+      return;
+    }
+    const UnitRecord r = unit_record(P, unit_pos(T, B, H, lam), descending);
+    put_record(U.list, bid, r.a, r.c);
     return;
   }
-  const int p = upper_index(T, B, lam / H);
-  const int nt = T[p + 1] - T[p];
-  const int r = lam - H * T[p];
-  const int h = r / nt;
-  const int tr = r - h * nt;
-  const int b = P.order[p];
-  const int64_t s = P.so[b];
-  const int64_t pb = P.pblk ? P.pblk[b] : 0;
-  rec[0] = make_int4(b, descending ? nt - 1 - tr : tr, h, (int)(P.so[b + 1] - s));
-  rec[1] = make_int4((int)s, P.rb_off[b], (int)(uint32_t)(uint64_t)pb, (int)(uint32_t)((uint64_t)pb >> 32));
+  if (bid >= n && bid < U.cap) put_record(U.list, bid, idle_a, idle_c);
+  if (blockIdx.x != 0) return;
+  for (int i = tid; i < kSmallUnits; i += kUnitThreads) hist[i] = 0;
+  if (tid == 0) smax = 0;
+  // each thread's units, decoded once (their loads overlap)
+  UnitPos up[kUnitsPerThread];
+  UnitRecord rec[kUnitsPerThread];
+#pragma unroll
+  for (int i = 0; i < kUnitsPerThread; ++i) {
+    const int lam = tid + i * kUnitThreads;
+    if (lam < n) {
+      up[i] = unit_pos(T, B, H, lam);
+      rec[i] = unit_record(P, up[i], descending);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kUnitsPerThread; ++i)
+    if (tid + i * kUnitThreads < n) atomicMax(&smax, up[i].nt);
+  __syncthreads();
+  const int maxnt = smax;
+  // estimate rank: 0 = heaviest; < maxnt <= n <= kSmallUnits
+  int key[kUnitsPerThread];
+#pragma unroll
+  for (int i = 0; i < kUnitsPerThread; ++i) {
+    const int t = descending ? up[i].nt - 1 - up[i].tr : up[i].tr;
+    key[i] = descending ? maxnt - 1 - t : maxnt - up[i].nt + t;
+    if (tid + i * kUnitThreads < n) atomicAdd(&hist[key[i]], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the histogram: thread tid owns bins [4 tid, 4 tid + 4)
+  constexpr int kRun = kSmallUnits / kUnitThreads;
+  int v[kRun], sum = 0;
+#pragma unroll
+  for (int i = 0; i < kRun; ++i) {
+    v[i] = hist[tid * kRun + i];
+    sum += v[i];
+  }
+  const int lane = tid & 63, w = tid >> 6;
+  int incl = sum;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) part[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int j = 0; j < w; ++j) base += part[j];
+  int run = base + incl - sum;
+#pragma unroll
+  for (int i = 0; i < kRun; ++i) {
+    hist[tid * kRun + i] = run;
+    run += v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kUnitsPerThread; ++i) {
+    if (tid + i * kUnitThreads < n) {
+      const int pos = atomicAdd(&hist[key[i]], 1);
+      put_record(U.list, pos, rec[i].a, rec[i].c);
+    }
+  }
 }
 
 // One wave per row block: envelopes of every interval.
@@ -317,11 +433,10 @@ hipError_t launch_prep(const Prep& P, const int64_t* seq_offsets, const int32_t*
 
 hipError_t launch_units(const Prep& P, const Units& U, int tile, int descending, int H,
                         int count_slot, hipStream_t stream) {
-  const int threads = 256;
-  const int blocks = (U.cap + threads - 1) / threads;
+  const int blocks = (U.cap + kUnitThreads - 1) / kUnitThreads;
   ProfScope ps(stream, "k_units");
-  hipLaunchKernelGGL(k_units, dim3(blocks > 0 ? blocks : 1), dim3(threads), 0, stream, P, U, tile,
-                     descending, H, count_slot);
+  hipLaunchKernelGGL(k_units, dim3(blocks > 0 ? blocks : 1), dim3(kUnitThreads), 0, stream, P, U,
+                     tile, descending, H, count_slot);
   return hipGetLastError();
 }
 
