@@ -14,8 +14,12 @@ head, over unmasked pairs only.  Also reported: per-step median and minimum
 over 3 further runs and the spread of their medians (step_stats), the
 targets-only mode (one candidate row per sequence against full-length K/V),
 per-kernel times measured with HIP events on the launch stream during the
-timed steps, the roofline of the dominant kernel, and the fp64 CPU oracle's
-rate on a sample of sequences.
+timed steps, the roofline of the dominant kernel, the other workloads at their
+full sizes (per_workload: SLA 1k / 2k, three-interval, OneRank, ragged, L=4086,
+each with its effective TFLOP/s and its fractions of the MFMA and HBM peaks),
+and the fp64 CPU oracle: its rate on a sample of the headline workload
+(cpu_baseline) and, under cpu_baseline.runs, timed in full on the small
+workloads and on samples of the others, with the host it ran on.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -97,9 +101,11 @@ def run_steps(hj, t, cfg, n, targets=False, pstore=None):
 
 
 def timed(hj, torch, t, cfg, steps, targets=False, pstore=None):
+    """ms per step over `steps` steps (a HIP event pair around them, nothing
+    else recorded), then the same steps again with the library's per-kernel
+    event pairs on, for the per-kernel times (those events add small gaps
+    between kernels, so the step time is not taken from that pass)."""
     torch.cuda.synchronize()
-    hj.profile_reset()
-    hj.profile_enable(True)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
@@ -108,6 +114,10 @@ def timed(hj, torch, t, cfg, steps, targets=False, pstore=None):
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    hj.profile_reset()
+    hj.profile_enable(True)
+    run_steps(hj, t, cfg, steps, targets, pstore)
+    torch.cuda.synchronize()
     hj.profile_enable(False)
     prof = hj.profile_read()
     return e0.elapsed_time(e1) / steps, wall, prof
@@ -156,6 +166,145 @@ def step_stats(hj, torch, t, cfg, steps, runs, pstore):
             "spread_pct": round(100.0 * (max(med) - min(med)) / min(med), 2)}
 
 
+# workloads measured beside the headline one (each at its own full size, same
+# entry points and backward path as the headline run)
+EXTRA_WORKLOADS = ("sla_1k", "sla_2k", "three_interval", "onerank", "hstu_ragged", "hstu_4086")
+
+
+def tensor_bytes(T, H, D):
+    """Algorithmic HBM bytes of one fwd+bwd: the forward reads q, k, v and
+    writes o; the backward reads q, k, v, dO and writes dq, dk, dv (bf16)."""
+    return 11.0 * T * H * D * 2
+
+
+def measure_workload(hj, torch, name, device, steps, dq_path):
+    """fwd+bwd of one named workload at full size: ms per step (HIP events),
+    fwd / bwd split, effective TFLOP/s (14 D per visible pair), fraction of
+    the bf16 MFMA peak and of HBM bandwidth (algorithmic bytes), per-kernel
+    times."""
+    cfg = wl.workload(name)
+    H, D = cfg["H"], cfg["D"]
+    t, off = make_inputs(cfg, device)
+    T = int(off[-1])
+    _, pairs_t = hj.visible_counts(t["off"], t["func"], T)
+    pairs = int(pairs_t.item())
+    pstore = None
+    if dq_path == "stored_p":
+        pstore = torch.empty(hj.pstore_bytes(t["off"], H), dtype=torch.uint8, device=device)
+    run_steps(hj, t, cfg, 2, pstore=pstore)
+    ms, _, prof = timed(hj, torch, t, cfg, steps, pstore=pstore)
+    split = split_ms(hj, torch, t, cfg, steps, pstore)
+    flops = 14.0 * D * H * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = tensor_bytes(T, H, D) / (ms * 1e-3) / 1e9
+    out = {"batch": len(cfg["lengths"]), "tokens": T, "heads": H, "head_dim": D,
+           "max_len": int(cfg["max_len"]), "visible_pairs_per_head": pairs,
+           "dq_path": dq_path, "ms_per_step": round(ms, 4), "split_ms": split,
+           "tflops_effective": round(tflops, 2),
+           "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+           "algorithmic_gb": round(tensor_bytes(T, H, D) / 1e9, 3),
+           "gbs_algorithmic": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+           "kernels_ms": {k: round(m / max(c, 1), 4) for k, (c, m) in sorted(prof.items())}}
+    del t, pstore
+    torch.cuda.empty_cache()
+    return out
+
+
+def host_info():
+    """The host the CPU baseline ran on: logical CPUs, CPUs this process may
+    use, the CPU model and the OpenMP thread count the oracle runs with."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    omp = None
+    try:
+        import ctypes
+
+        omp = int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
+    except (OSError, AttributeError):
+        pass
+    return {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "cpu_model": model, "omp_threads": omp,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
+def oracle_time(torch, cfg, t, off, seqs, targets=None):
+    """fwd+bwd of the fp64 oracle on the sequences `seqs` (all of them when
+    None): seconds and the effective flops (14 D per visible pair) it did."""
+    import oracle
+
+    if seqs is None:
+        seqs = list(range(len(cfg["lengths"])))
+    rows, sub_off = oracle.subset(off, seqs)
+    rows_t = torch.from_numpy(rows).to(t["k"].device)
+    to64 = lambda x: x.index_select(0, rows_t).float().cpu().numpy().astype(np.float64)  # noqa: E731
+    k, v = to64(t["k"]), to64(t["v"])
+    if targets is not None:
+        sel = torch.tensor(seqs, device=t["k"].device)
+        q = t["q"].index_select(0, sel).float().cpu().numpy().astype(np.float64)
+        do = t["do"].index_select(0, sel).float().cpu().numpy().astype(np.float64)
+        tr = targets[seqs]
+    else:
+        q, do, tr = to64(t["q"]), to64(t["do"]), None
+    func = np.ascontiguousarray(t["func"].cpu().numpy()[:, rows])
+    orc = oracle.default()
+    _, pairs = orc.visible_counts(sub_off, func, tr)
+    t0 = time.perf_counter()
+    orc.fwd(q, k, v, sub_off, func, cfg["alpha"], cfg["max_len"], tr)
+    orc.bwd(q, k, v, do, sub_off, func, cfg["alpha"], cfg["max_len"], tr)
+    dt = time.perf_counter() - t0
+    return dt, 14.0 * cfg["D"] * cfg["H"] * pairs
+
+
+def cpu_record(torch, device):
+    """The oracle timed in full on the small workloads and on samples of the
+    large ones (scaled by visible pairs, which the oracle's work is
+    proportional to): seconds, effective TFLOP/s, and for samples the
+    extrapolated full time."""
+    runs = {}
+    for name, sample in (("tiny_fp32", None), ("sla_1k", None), ("sla_2k", None),
+                         ("hstu_2663_targets_only", None), ("three_interval", 8)):
+        base = "hstu_2663" if name.startswith("hstu_2663") else name
+        cfg = wl.workload(base)
+        targets = name.endswith("targets_only")
+        if cfg["dtype"] == "fp32":
+            lengths = cfg["lengths"]
+            off = wl.offsets_from_lengths(lengths)
+            T = int(off[-1])
+            mk = lambda sh, sd: torch.from_numpy(wl.normal_f32(sh, sd)).to(device)  # noqa: E731
+            sh = (T, cfg["H"], cfg["D"])
+            t = {"q": mk(sh, 11), "k": mk(sh, 12), "v": mk(sh, 13), "do": mk(sh, 14),
+                 "func": torch.from_numpy(cfg["func"](lengths, cfg["nfunc"])).to(device)}
+        else:
+            t, off = make_inputs(cfg, device, targets=targets)
+        lengths = cfg["lengths"]
+        seqs = None
+        if sample:
+            seqs = [int(i) for i in np.linspace(0, len(lengths) - 1, sample)]
+        dt, flops = oracle_time(torch, cfg, t, off, seqs,
+                                wl.targets_last(lengths) if targets else None)
+        rec = {"seconds": round(dt, 3), "tflops_effective": round(flops / dt / 1e12, 6),
+               "sequences": len(seqs) if seqs else len(lengths), "of": len(lengths)}
+        if seqs:
+            import hstu_jagged_masked_amd as hj
+
+            f_all = torch.from_numpy(cfg["func"](lengths, cfg["nfunc"])).to(device)
+            _, tot = hj.visible_counts(torch.from_numpy(off).to(device), f_all, int(off[-1]))
+            full_flops = 14.0 * cfg["D"] * cfg["H"] * int(tot.item())
+            rec["extrapolated_full_seconds"] = round(dt * full_flops / flops, 1)
+        runs[name] = rec
+        log(f"[bench] cpu oracle {name}: {rec}")
+        del t
+    torch.cuda.empty_cache()
+    return runs
+
+
 def cpu_baseline(cfg, t, off, nseq):
     """The fp64 oracle on the first `nseq` sequences (fwd + bwd), host cores."""
     import oracle
@@ -172,12 +321,18 @@ def cpu_baseline(cfg, t, off, nseq):
     orc.bwd(q, k, v, do, sub_off, func, cfg["alpha"], cfg["max_len"])
     dt = time.perf_counter() - t0
     flops = 14.0 * cfg["D"] * cfg["H"] * pairs
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, nseq * cfg["H"]),
+    info = host_info()
+    threads = info["omp_threads"] or int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    full_flops = 14.0 * cfg["D"] * cfg["H"] * float(np.sum(cfg["lengths"] * (cfg["lengths"] + 1) // 2))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s",
+            # the oracle runs one OpenMP thread per (sequence, head) unit at most
+            "cores": min(threads, nseq * cfg["H"]),
             "kind": "oracle",
             "sample": f"fp64 oracle fwd+bwd on {nseq} of {len(cfg['lengths'])} sequences "
                       f"(L={int(cfg['lengths'][0])}, all {cfg['H']} heads), {dt:.2f} s, "
-                      f"effective flops 14*D per visible pair"}
+                      f"effective flops 14*D per visible pair",
+            "extrapolated_full_seconds": round(dt * full_flops / flops, 1),
+            **info}
 
 
 def main():
@@ -193,6 +348,9 @@ def main():
                     help="dQ path of the backward: from stored P (needs ~2 bytes per (row, "
                          "column) pair of each sequence per head of HBM) or recomputing the "
                          "scores; the run fails rather than switch paths when memory is short")
+    ap.add_argument("--no-extra", dest="extra", action="store_false",
+                    help="skip the other workloads (SLA, three-interval, OneRank, ragged, "
+                         "L=4086) and the full CPU record")
     ap.add_argument("--calib-copy-mib", type=int, default=1024,
                     help="size of a plain device-to-device copy run once before timing; "
                          "counter runs scale HBM byte counters by it (0 disables it)")
@@ -261,6 +419,7 @@ def main():
                 "traffic": measured_traffic(dom)}
 
     del pstore
+    torch.cuda.empty_cache()
     # targets-only mode on the same K/V
     tt, _ = make_inputs(cfg, device, targets=True)
     tt["k"], tt["v"] = t["k"], t["v"]
@@ -299,6 +458,21 @@ def main():
         log(f"[bench] cpu oracle baseline on {args.cpu_seqs} sequences ...")
         cpu = cpu_baseline(cfg, t, off, args.cpu_seqs)
         log(f"[bench] cpu oracle: {cpu['value']:.6f} TFLOP/s")
+    del t
+    torch.cuda.empty_cache()
+
+    per_workload = {}
+    if args.extra:
+        for name in EXTRA_WORKLOADS:
+            if name == args.workload:
+                continue
+            per_workload[name] = measure_workload(hj, torch, name, device,
+                                                  min(args.steps, 10),
+                                                  "stored_p" if use_p else "recompute")
+            log(f"[bench] {name}: {per_workload[name]['ms_per_step']} ms/step, "
+                f"{per_workload[name]['tflops_effective']} TFLOP/s")
+        if cpu is not None:
+            cpu["runs"] = cpu_record(torch, device)
 
     out = {
         "metric": METRIC,
@@ -328,6 +502,7 @@ def main():
         "cpu_baseline": cpu,
         "targets_only": targets,
         "nfunc_pad_cost": pad,
+        "per_workload": per_workload,
         "kernels": kernels,
         "wall_s_timed": round(wall, 3),
     }
