@@ -92,15 +92,27 @@ def make_inputs(cfg, device, targets=False):
     return t, off
 
 
-def run_steps(hj, t, cfg, n, targets=False, pstore=None):
+def run_steps(hj, t, cfg, n, targets=False, pstore=None, host_offsets=None):
     tr = t.get("tr") if targets else None
     for _ in range(n):
         hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], t["func"], cfg["alpha"], cfg["max_len"], tr)
         hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], t["func"], cfg["alpha"],
-                    cfg["max_len"], tr, pstore=pstore)
+                    cfg["max_len"], tr, pstore=pstore, host_offsets=host_offsets)
 
 
-def timed(hj, torch, t, cfg, steps, targets=False, pstore=None):
+def pstore_runs(lengths, H, budget):
+    """Runs the bounded stored-P backward cuts a batch into (consecutive
+    sequences, each run as long as the buffer holds its stored P)."""
+    runs, need = 1, 0
+    for L in lengths:
+        one = -(-int(L) // 128) * -(-int(L) // 32) * 8192 * H
+        if need + one > budget:
+            runs, need = runs + 1, 0
+        need += one
+    return runs
+
+
+def timed(hj, torch, t, cfg, steps, targets=False, pstore=None, host_offsets=None):
     """ms per step over `steps` steps (a HIP event pair around them, nothing
     else recorded), then the same steps again with the library's per-kernel
     event pairs on, for the per-kernel times (those events add small gaps
@@ -110,13 +122,13 @@ def timed(hj, torch, t, cfg, steps, targets=False, pstore=None):
     e1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     e0.record()
-    run_steps(hj, t, cfg, steps, targets, pstore)
+    run_steps(hj, t, cfg, steps, targets, pstore, host_offsets)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     hj.profile_reset()
     hj.profile_enable(True)
-    run_steps(hj, t, cfg, steps, targets, pstore)
+    run_steps(hj, t, cfg, steps, targets, pstore, host_offsets)
     torch.cuda.synchronize()
     hj.profile_enable(False)
     prof = hj.profile_read()
@@ -348,6 +360,9 @@ def main():
                     help="dQ path of the backward: from stored P (needs ~2 bytes per (row, "
                          "column) pair of each sequence per head of HBM) or recomputing the "
                          "scores; the run fails rather than switch paths when memory is short")
+    ap.add_argument("--pstore-budget-gb", type=float, default=4.0,
+                    help="also time the stored-P backward over a buffer of this many GiB, in "
+                         "runs of sequences (0: skip)")
     ap.add_argument("--no-extra", dest="extra", action="store_false",
                     help="skip the other workloads (SLA, three-interval, OneRank, ragged, "
                          "L=4086) and the full CPU record")
@@ -420,6 +435,23 @@ def main():
 
     del pstore
     torch.cuda.empty_cache()
+    # the stored-P backward over a bounded buffer, in runs of sequences
+    chunked = None
+    if use_p and args.pstore_budget_gb > 0:
+        budget = int(args.pstore_budget_gb * (1 << 30)) // 256 * 256
+        runs = pstore_runs(cfg["lengths"], H, budget)
+        pb = torch.empty(budget, dtype=torch.uint8, device=device)
+        run_steps(hj, t, cfg, 2, pstore=pb, host_offsets=off)
+        c_ms, _, c_prof = timed(hj, torch, t, cfg, args.steps, pstore=pb, host_offsets=off)
+        log(f"[bench] stored P in {runs} runs over {args.pstore_budget_gb} GiB: {c_ms:.3f} ms/step")
+        chunked = {"budget_gib": args.pstore_budget_gb, "runs": runs,
+                   "ms_per_step": round(c_ms, 4),
+                   "effective_tflops": round(flops_eff / (c_ms * 1e-3) / 1e12, 2),
+                   "vs_whole_batch_buffer": round(c_ms / ms, 4),
+                   "kernels_ms_per_step": {k: round(v[1] / args.steps, 4)
+                                           for k, v in sorted(c_prof.items())}}
+        del pb
+        torch.cuda.empty_cache()
     # targets-only mode on the same K/V
     tt, _ = make_inputs(cfg, device, targets=True)
     tt["k"], tt["v"] = t["k"], t["v"]
@@ -501,6 +533,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "targets_only": targets,
+        "pstore_bounded": chunked,
         "nfunc_pad_cost": pad,
         "per_workload": per_workload,
         "kernels": kernels,

@@ -79,6 +79,9 @@ def library() -> ctypes.CDLL:
     lib.hstu_attn_bwd_pstore.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i32, i32, P, i32, f32,
                                          i64, P, sz, P, sz, P]
     lib.hstu_attn_bwd_pstore.restype = i32
+    lib.hstu_attn_bwd_pstore_chunked.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i32, i32, P,
+                                                 i32, f32, i64, P, sz, P, sz, P]
+    lib.hstu_attn_bwd_pstore_chunked.restype = i32
     lib.hstu_attn_pstore_bytes.argtypes = [P, i64, i64, i32]
     lib.hstu_attn_pstore_bytes.restype = sz
     lib.hstu_profile_enable.argtypes = [i32]
@@ -92,7 +95,8 @@ def library() -> ctypes.CDLL:
 
 
 EXPORTED = ("hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size", "hstu_attn_fwd",
-            "hstu_attn_fwd_noalloc", "hstu_attn_bwd", "hstu_attn_bwd_pstore", "hstu_attn_pstore_bytes",
+            "hstu_attn_fwd_noalloc", "hstu_attn_bwd", "hstu_attn_bwd_pstore", "hstu_attn_bwd_pstore_chunked",
+            "hstu_attn_pstore_bytes",
             "hstu_attn_visible_counts", "hstu_attn_check_inputs",
             "hstu_profile_enable", "hstu_profile_read", "hstu_profile_reset")
 
@@ -196,11 +200,15 @@ def pstore_bytes(seq_offsets, H) -> int:
     return int(library().hstu_attn_pstore_bytes(ctypes.c_void_p(off.data_ptr()), B, total, int(H)))
 
 
-def attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None, pstore=None):
+def attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None, pstore=None,
+             host_offsets=None):
     """Backward.  With ``pstore`` (a CUDA uint8 tensor of at least
     ``pstore_bytes(seq_offsets, H)`` bytes; bf16, D = 128, full-length mode) the
     stored-P path runs: no recomputation of the scores for dQ.  The size is
-    checked on the device: with a smaller buffer dq comes back as NaN."""
+    checked on the device: with a smaller buffer dq comes back as NaN.
+    With ``host_offsets`` as well (a CPU int64 copy of seq_offsets), ``pstore``
+    may be of any size that holds the largest sequence's P: the batch runs in
+    runs of sequences that fit it, with the same outputs."""
     B, total, H, D, nfunc = _common(q, k, seq_offsets, func, target_rows)
     for t in (q, k, v, dout):
         if not t.is_contiguous() or t.dtype != k.dtype:
@@ -216,6 +224,16 @@ def attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None,
             raise ValueError("the stored-P backward needs bf16 and full-length mode")
         if pstore.dtype != torch.uint8 or not pstore.is_contiguous():
             raise ValueError("pstore must be a contiguous uint8 tensor")
+        if host_offsets is not None:
+            ho = torch.as_tensor(host_offsets, dtype=torch.int64, device="cpu").contiguous()
+            if ho.numel() != B + 1:
+                raise ValueError("host_offsets must hold B + 1 offsets")
+            _check(library().hstu_attn_bwd_pstore_chunked(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                _ptr(seq_offsets), ctypes.c_void_p(ho.data_ptr()), B, total, H, D, _ptr(func),
+                nfunc, float(alpha), int(max_len), _ptr(ws), ws.numel(), _ptr(pstore),
+                pstore.numel(), _stream(k.device)))
+            return dq, dk, dv
         _check(library().hstu_attn_bwd_pstore(
             _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
             _ptr(seq_offsets), B, total, H, D, _ptr(func), nfunc, float(alpha), int(max_len),

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -97,6 +98,8 @@ Prep prep_view(const Plan& p, void* ws, int B, int64_t total) {
   P.pblk = p.off_pblk ? reinterpret_cast<int64_t*>(base + p.off_pblk) : nullptr;
   P.B = B;
   P.total = total;
+  P.row_lo = 0;
+  P.row_hi = total;
   P.nrb_cap = p.nrb_cap;
   return P;
 }
@@ -346,16 +349,13 @@ extern "C" size_t hstu_attn_pstore_bytes(const int64_t* seq_offsets, int64_t B, 
   return (size_t)blocks * H * kPBlockBytes;
 }
 
-extern "C" int hstu_attn_bwd_pstore(const void* q, const void* k, const void* v, const void* dout,
-                                    void* dq, void* dk, void* dv, const int64_t* seq_offsets,
-                                    int64_t B, int64_t total, int H, int D, const int32_t* func,
-                                    int nfunc, float alpha, int64_t max_len, void* workspace,
-                                    size_t workspace_bytes, void* pstore, size_t pstore_bytes,
-                                    void* stream) {
-  Plan plan;
-  int st = validate(plan, 1, HSTU_BF16, B, total, H, D, nfunc, alpha, max_len, seq_offsets, func,
-                    nullptr, workspace, workspace_bytes);
-  if (st) return st;
+namespace {
+
+// Checks shared by the stored-P entry points (after validate()).
+int check_pstore_args(int64_t total, int D, const void* q, const void* k, const void* v,
+                      const void* dout, const void* dq, const void* dk, const void* dv,
+                      const void* pstore) {
+  int st;
   if (D != 128)
     return fail(HSTU_ERR_UNSUPPORTED, "the stored-P backward needs D = 128, got %d", D);
   if ((st = check_tensor(q, total, "q")) || (st = check_tensor(k, total, "k")) ||
@@ -366,23 +366,108 @@ extern "C" int hstu_attn_bwd_pstore(const void* q, const void* k, const void* v,
   if (total > 0 && !pstore) return fail(HSTU_ERR_INVALID, "pstore is NULL");
   if (reinterpret_cast<uintptr_t>(pstore) & 255u)
     return fail(HSTU_ERR_INVALID, "pstore must be 256-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const float inv_max_len = (float)(1.0 / (double)max_len);
-  Prep P = prep_view(plan, workspace, (int)B, total);
+  return HSTU_OK;
+}
+
+// The stored-P backward of the `nb` sequences whose offsets start at
+// `seq_offsets`, their rows clamped into [row_lo, row_hi]: prep, both unit
+// lists and the two passes, with grids sized for those rows.
+int bwd_pstore_run(const Plan& plan, void* workspace, const void* q, const void* k,
+                   const void* v, const void* dout, void* dq, void* dk, void* dv,
+                   const int64_t* seq_offsets, int64_t nb, int64_t total, int64_t row_lo,
+                   int64_t row_hi, int H, const int32_t* func, int nfunc, float alpha,
+                   float inv_max_len, void* pstore, size_t pstore_bytes, hipStream_t s) {
+  Prep P = prep_view(plan, workspace, (int)nb, total);
+  P.row_lo = row_lo;
+  P.row_hi = row_hi;
+  const int64_t rows = row_hi - row_lo;
+  P.nrb_cap = (int)std::min<int64_t>(plan.nrb_cap, cdiv64(rows, kRB) + nb);
   hipError_t e = launch_prep(P, seq_offsets, nullptr, func, nfunc, s);
   if (e != hipSuccess) return device_fail(e, "prep");
   // The size the lengths need is known on the device only; the kernels
   // compare it with pstore_bytes themselves (every P access is range-checked
   // against the buffer, and dq is written as NaN when the buffer is too
-  // small), so nothing here waits for the device.
-  Units Ukv = units_view(workspace, plan.off_units_b, plan.cap_b);
-  Units Uq = units_view(workspace, plan.off_units_c, plan.cap_c);
+  // small), so nothing here waits for the device.  Whatever the offsets
+  // hold, the sanitized lengths sum to `rows`, so the grids below hold
+  // every unit.
+  const int cap = std::min(plan.cap_b, round8((int64_t)H * (cdiv64(rows, 128) + nb)));
+  Units Ukv = units_view(workspace, plan.off_units_b, cap);
+  Units Uq = units_view(workspace, plan.off_units_c, cap);
   e = launch_units(P, Ukv, 128, 0, H, kSlotKvUnits, s);
   if (e == hipSuccess) e = launch_units(P, Uq, 128, 1, H, kSlotQUnits, s);
   if (e != hipSuccess) return device_fail(e, "unit list");
   e = launch_mfma_bwd(q, k, v, dout, dq, dk, dv, P, Ukv, Uq, H, func, nfunc, alpha, inv_max_len,
                       static_cast<uint16_t*>(pstore), (uint64_t)pstore_bytes, s);
   if (e != hipSuccess) return device_fail(e, "backward");
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" int hstu_attn_bwd_pstore(const void* q, const void* k, const void* v, const void* dout,
+                                    void* dq, void* dk, void* dv, const int64_t* seq_offsets,
+                                    int64_t B, int64_t total, int H, int D, const int32_t* func,
+                                    int nfunc, float alpha, int64_t max_len, void* workspace,
+                                    size_t workspace_bytes, void* pstore, size_t pstore_bytes,
+                                    void* stream) {
+  Plan plan;
+  int st = validate(plan, 1, HSTU_BF16, B, total, H, D, nfunc, alpha, max_len, seq_offsets, func,
+                    nullptr, workspace, workspace_bytes);
+  if (st) return st;
+  if ((st = check_pstore_args(total, D, q, k, v, dout, dq, dk, dv, pstore))) return st;
+  return bwd_pstore_run(plan, workspace, q, k, v, dout, dq, dk, dv, seq_offsets, B, total, 0,
+                        total, H, func, nfunc, alpha, (float)(1.0 / (double)max_len), pstore,
+                        pstore_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int hstu_attn_bwd_pstore_chunked(const void* q, const void* k, const void* v,
+                                         const void* dout, void* dq, void* dk, void* dv,
+                                         const int64_t* seq_offsets, const int64_t* host_offsets,
+                                         int64_t B, int64_t total, int H, int D,
+                                         const int32_t* func, int nfunc, float alpha,
+                                         int64_t max_len, void* workspace, size_t workspace_bytes,
+                                         void* pstore, size_t pstore_bytes, void* stream) {
+  Plan plan;
+  int st = validate(plan, 1, HSTU_BF16, B, total, H, D, nfunc, alpha, max_len, seq_offsets, func,
+                    nullptr, workspace, workspace_bytes);
+  if (st) return st;
+  if ((st = check_pstore_args(total, D, q, k, v, dout, dq, dk, dv, pstore))) return st;
+  if (!host_offsets) return fail(HSTU_ERR_INVALID, "host_offsets is NULL");
+  if (host_offsets[0] != 0 || host_offsets[B] != total)
+    return fail(HSTU_ERR_INVALID, "host_offsets must run from 0 to total = %lld",
+                (long long)total);
+  for (int64_t b = 0; b < B; ++b)
+    if (host_offsets[b + 1] < host_offsets[b])
+      return fail(HSTU_ERR_INVALID, "host_offsets decrease at sequence %lld", (long long)b);
+  // runs of consecutive sequences whose stored P fits the buffer, each cut
+  // as long as it can be; every run is checked before the first launch, so
+  // an error leaves the outputs untouched
+  auto seq_bytes = [&](int64_t b) {
+    return (uint64_t)pstore_seq_blocks(host_offsets[b + 1] - host_offsets[b]) * (uint64_t)H *
+           kPBlockBytes;
+  };
+  auto run_end = [&](int64_t b0) {
+    uint64_t need = 0;
+    int64_t b1 = b0;
+    while (b1 < B && need + seq_bytes(b1) <= (uint64_t)pstore_bytes) need += seq_bytes(b1++);
+    return b1;
+  };
+  for (int64_t b0 = 0, b1; b0 < B; b0 = b1) {
+    b1 = run_end(b0);
+    if (b1 == b0)
+      return fail(HSTU_ERR_INVALID,
+                  "sequence %lld needs %llu bytes of stored P; the buffer holds %zu", (long long)b0,
+                  (unsigned long long)seq_bytes(b0), pstore_bytes);
+  }
+  const float inv_max_len = (float)(1.0 / (double)max_len);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t b0 = 0, b1; b0 < B; b0 = b1) {
+    b1 = run_end(b0);
+    st = bwd_pstore_run(plan, workspace, q, k, v, dout, dq, dk, dv, seq_offsets + b0, b1 - b0,
+                        total, host_offsets[b0], host_offsets[b1], H, func, nfunc, alpha,
+                        inv_max_len, pstore, pstore_bytes, s);
+    if (st) return st;
+  }
   return HSTU_OK;
 }
 

@@ -60,8 +60,11 @@ struct Prep {
   int64_t* pblk;       // [B+1] prefix of ceil(L/128)*ceil(L/32) (stored-P blocks per
                        // head of each sequence, original order); null when not planned
   int B;
-  int64_t total;
-  int nrb_cap;         // capacity of row blocks: ceil(total/64) + B
+  int64_t total;       // rows of q, k, v and func (the func row stride)
+  int64_t row_lo;      // the offsets are clamped into [row_lo, row_hi], the first
+  int64_t row_hi;      // set to row_lo and the last to row_hi (0 and total for a
+                       // whole batch, a run's rows for a run of its sequences)
+  int nrb_cap;         // capacity of row blocks: ceil((row_hi - row_lo)/64) + B
 };
 
 struct Units {

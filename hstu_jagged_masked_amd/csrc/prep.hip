@@ -75,30 +75,31 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Prep P, const int64_t* __
   __shared__ int sflags;
   const int tid = threadIdx.x;
   const int B = P.B;
-  const int64_t total = P.total;
   if (tid == 0) sflags = 0;
   for (int i = tid; i < kHistBins; i += kPrepThreads) hist[i] = 0;
   __syncthreads();
 
-  // 1. sanitized offsets: clamp into [0, total] and take a running maximum.
+  // 1. sanitized offsets: clamp into [lo, hi] (0 and total for a whole
+  // batch) and take a running maximum.
+  const int64_t lo = P.row_lo, hi = P.row_hi;
   int flags = 0;
-  int64_t run = 0;
+  int64_t run = lo;
   for (int base = 0; base <= B; base += kPrepThreads) {
     const int b = base + tid;
-    int64_t x = 0;
+    int64_t x = lo;
     if (b <= B) {
       int64_t raw = off[b];
-      if (b == 0 && raw != 0) flags |= kFlagOffsetsStart;
-      if (b == B && raw != total) flags |= kFlagOffsetsEnd;
-      if (raw < 0 || raw > total) flags |= kFlagOffsetsOrder;
+      if (b == 0 && raw != lo) flags |= kFlagOffsetsStart;
+      if (b == B && raw != hi) flags |= kFlagOffsetsEnd;
+      if (raw < lo || raw > hi) flags |= kFlagOffsetsOrder;
       if (b > 0 && raw < off[b - 1]) flags |= kFlagOffsetsOrder;
-      x = raw < 0 ? 0 : (raw > total ? total : raw);
+      x = raw < lo ? lo : (raw > hi ? hi : raw);
     }
     int64_t chunk_max;
     int64_t m = block_inclusive_scan(x, scan64, &chunk_max, MaxOp());
     m = m > run ? m : run;
-    if (b == 0) m = 0;
-    if (b == B) m = total;
+    if (b == 0) m = lo;
+    if (b == B) m = hi;
     if (b <= B) P.so[b] = m;
     run = chunk_max > run ? chunk_max : run;
   }

@@ -154,6 +154,32 @@ int hstu_attn_bwd_pstore(const void* q, const void* k, const void* v, const void
  * [0, total], running maximum).  Returns 0 for unsupported sizes. */
 size_t hstu_attn_pstore_bytes(const int64_t* seq_offsets, int64_t B, int64_t total, int H);
 
+/* Stored-P backward with a buffer of any size the caller picks: the batch is
+ * cut into runs of consecutive sequences, each as long as the buffer holds
+ * its stored P (ceil(L/128) * ceil(L/32) * 8192 * H bytes per sequence), and
+ * hstu_attn_bwd_pstore's work runs once per run on `stream`, each run
+ * reusing the buffer.  The outputs are bitwise those of hstu_attn_bwd_pstore
+ * with a buffer that holds the whole batch; the footprint is pstore_bytes,
+ * whatever the batch size (the pages' layer shapes reach 137 GB of stored P
+ * for the whole batch at L = 4086: MLCommons training PR #903, "Evidence").
+ * Each run launches its own prep and passes, so runs should hold many
+ * sequences (a buffer of a few GB at the pages' shapes).
+ * host_offsets: a HOST copy of seq_offsets (int64 [B+1], 0 = first <= ... <=
+ * last = total), read before anything is enqueued to cut the runs; the
+ * device offsets of each run are clamped into that run's rows, so a device
+ * copy that disagrees with it gives wrong gradients but no access outside
+ * the tensors.  Fails with HSTU_ERR_INVALID, before enqueueing anything, when
+ * host_offsets is malformed or one sequence alone needs more than
+ * pstore_bytes.  Other arguments, the workspace (hstu_attn_workspace_size
+ * with is_bwd = 1) and the asynchronous, deterministic behaviour are those
+ * of hstu_attn_bwd_pstore. */
+int hstu_attn_bwd_pstore_chunked(const void* q, const void* k, const void* v, const void* dout,
+                                 void* dq, void* dk, void* dv, const int64_t* seq_offsets,
+                                 const int64_t* host_offsets, int64_t B, int64_t total, int H,
+                                 int D, const int32_t* func, int nfunc, float alpha,
+                                 int64_t max_len, void* workspace, size_t workspace_bytes,
+                                 void* pstore, size_t pstore_bytes, void* stream);
+
 /* Visible-column count |V_i| of every query row: counts is int32 [total]
  * (or [B] with target_rows), total_pairs a device int64 receiving their sum.
  * Either output may be NULL.  Integer work: exact. */

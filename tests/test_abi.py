@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size",
                             "hstu_attn_fwd", "hstu_attn_fwd_noalloc", "hstu_attn_bwd",
-                            "hstu_attn_bwd_pstore",
+                            "hstu_attn_bwd_pstore", "hstu_attn_bwd_pstore_chunked",
                             "hstu_attn_pstore_bytes", "hstu_attn_visible_counts",
                             "hstu_attn_check_inputs", "hstu_profile_enable",
                             "hstu_profile_read", "hstu_profile_reset"])
@@ -160,6 +160,31 @@ def test_bwd_pstore_rejects_bad_arguments(lib):
     assert call(pstore=None) == -1 and "pstore is NULL" in lib.hstu_last_error().decode()
     assert call(pstore=P(FAKE + 16)) == -1 and "256-byte" in lib.hstu_last_error().decode()
     assert call(ws_bytes=16) == -3
+
+
+def test_bwd_pstore_chunked_rejects_bad_arguments(lib):
+    """Malformed host offsets, and a buffer smaller than one sequence's stored
+    P, are refused on the host before anything is enqueued (the library never
+    touches the fake device pointers)."""
+    P = ctypes.c_void_p
+    f = P(FAKE)
+
+    def call(offs, pstore_bytes, H=2, host=True):
+        keep, off = _host_offsets(offs)
+        st = lib.hstu_attn_bwd_pstore_chunked(
+            f, f, f, f, f, f, f, f, off if host else None, len(offs) - 1, offs[-1], H, 128, f, 5,
+            0.1, 8, f, 1 << 20, f, pstore_bytes, None)
+        return st, lib.hstu_last_error().decode()
+
+    st, msg = call([0, 100, 300], 1 << 30, host=False)
+    assert st == -1 and "host_offsets is NULL" in msg
+    st, msg = call([1, 100, 300], 1 << 30)
+    assert st == -1 and "from 0 to total" in msg
+    st, msg = call([0, 200, 100, 300], 1 << 30)
+    assert st == -1 and "decrease at sequence 1" in msg
+    # lengths 100, 200 at H = 2: 4 and 14 blocks of 8 KiB per head
+    st, msg = call([0, 100, 300], 14 * 2 * 8192 - 1)
+    assert st == -1 and "sequence 1 needs 229376 bytes" in msg
 
 
 def test_fwd_noalloc_rejects_sizes_beyond_its_array(lib):

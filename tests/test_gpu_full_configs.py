@@ -72,7 +72,9 @@ def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False, pstore=False)
     output element is written by one workgroup in a fixed order, so any
     difference is a race).  With `pstore`, the stored-P backward runs too (after
     the default one, on the same inputs) and is checked against the same
-    oracle values, and its dk, dv must equal the default path's bit for bit."""
+    oracle values, and its dk, dv must equal the default path's bit for bit;
+    run over a buffer of about a seventh of the batch's stored P, in runs of
+    sequences, it must reproduce its own outputs bit for bit."""
     t, off = device_inputs(cfg)
     func = torch.from_numpy(func_np).to(DEV)
     o = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], func, cfg["alpha"], cfg["max_len"])
@@ -97,7 +99,19 @@ def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False, pstore=False)
             for nm, a, b in zip(("dq", "dk", "dv"), gp, gp2):
                 assert torch.equal(a, b), f"{cfg['name']}.pstore.{nm}: second run differs"
             del gp2
+        # the same backward in runs of sequences sharing a buffer of about a
+        # seventh of the batch's need: bit for bit the one-run outputs
+        need = ps.numel()
         del ps
+        per_seq = max(-(-int(L) // 128) * -(-int(L) // 32) * 8192 * cfg["H"]
+                      for L in cfg["lengths"])
+        budget = max(per_seq, need // 7) // 256 * 256 + 256
+        ps = torch.empty(budget, dtype=torch.uint8, device=DEV)
+        gc = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
+                         cfg["max_len"], pstore=ps, host_offsets=torch.from_numpy(off))
+        for nm, a, b in zip(("dq", "dk", "dv"), gp, gc):
+            assert torch.equal(a, b), f"{cfg['name']}.pstore chunked ({budget} B).{nm} differs"
+        del ps, gc
         assert torch.equal(gp[1], dk) and torch.equal(gp[2], dv), "stored-P dk/dv differ"
     torch.cuda.synchronize()
     rows, sub_off = oracle.subset(off, seqs)

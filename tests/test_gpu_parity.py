@@ -338,6 +338,36 @@ def test_bf16_pstore_dk_dv_bitwise_equal_recompute_path(hj):
     assert err <= 2e-2 * dq0.float().abs().max().item()
 
 
+@pytest.mark.parametrize("name", ["causal_ragged", "random_nfunc9", "onerank", "sla",
+                                  "single_rows"])
+def test_bf16_pstore_chunked_bitwise(hj, name):
+    """The stored-P backward cut into runs of sequences that share one smaller
+    buffer gives bitwise the outputs of one run over a buffer for the whole
+    batch, at budgets from the largest sequence's need (most runs) up to the
+    whole batch; every P access stays inside the budget (a guard region after
+    it keeps its bytes)."""
+    lengths, fn, alpha, max_len = PSTORE_CASES[name]
+    # empty sequences at the ends (not for OneRank, whose mask follows its layout)
+    ls = np.array(list(lengths) if name == "onerank" else [0] + list(lengths) + [0, 0])
+    H = 2
+    off = wl.offsets_from_lengths(ls)
+    off_t = torch.from_numpy(off).to(DEV)
+    inp = make_inputs(ls, H, 128, "bf16", 35)
+    f = torch.from_numpy(fn(ls)).to(DEV)
+    args = (inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], off_t, f, alpha, max_len)
+    need = hj.pstore_bytes(off_t, H)
+    ref = hj.attn_bwd(*args, pstore=pstore_for(hj, off_t, H))
+    per_seq = [-(-int(L) // 128) * -(-int(L) // 32) * 8192 * H for L in ls]
+    for budget in sorted({max(per_seq), max(max(per_seq), need // 2), need}):
+        budget = max(budget, 256)
+        buf = torch.full((budget + (64 << 10),), 0x5A, dtype=torch.uint8, device=DEV)
+        got = hj.attn_bwd(*args, pstore=buf[:budget], host_offsets=torch.from_numpy(off))
+        torch.cuda.synchronize()
+        for r, g, nm in zip(ref, got, ("dq", "dk", "dv")):
+            assert torch.equal(r, g), f"{name} budget {budget}: {nm} differs"
+        assert bool((buf[budget:] == 0x5A).all()), f"{name} budget {budget}: guard overwritten"
+
+
 def test_bf16_pstore_buffer_too_small(hj):
     """A stored-P buffer smaller than the device offsets need: the call does
     not synchronize to find out; every P access stays inside the buffer (a
