@@ -187,23 +187,24 @@ extern "C" int hstu_attn_fwd(int dtype, const void* q, const void* k, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float inv_max_len = (float)(1.0 / (double)max_len);
   Prep P = prep_view(plan, workspace, (int)B, total);
-  hipError_t e = launch_prep(P, seq_offsets, target_rows, func, nfunc, s);
+  hipError_t e = launch_prep(P, seq_offsets, target_rows, s);
   if (e != hipSuccess) return device_fail(e, "prep");
   if (target_rows) {
     float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_partial);
-    Units U = units_view(workspace, plan.off_units_a, plan.cap_a);
-    e = launch_units(P, U, 128, 0, H, kSlotFwdUnits, s);
+    const UnitJob job{units_view(workspace, plan.off_units_a, plan.cap_a), 128, 0, kSlotFwdUnits};
+    e = launch_lists(P, nullptr, nfunc, &job, 1, H, s);
     if (e != hipSuccess) return device_fail(e, "unit list");
+    const Units& U = job.U;
     e = launch_targets_fwd(dtype, D, q, k, v, o, P, U, H, func, nfunc, alpha, inv_max_len,
                            target_rows, partial, s);
     if (e != hipSuccess) return device_fail(e, "targets-only forward");
     return HSTU_OK;
   }
   if (mfma_path(dtype, D)) {
-    Units U = units_view(workspace, plan.off_units_a, plan.cap_a);
-    e = launch_units(P, U, 128, 1, H, kSlotFwdUnits, s);
-    if (e != hipSuccess) return device_fail(e, "unit list");
-    e = launch_mfma_fwd(q, k, v, o, P, U, H, func, nfunc, alpha, inv_max_len, s);
+    const UnitJob job{units_view(workspace, plan.off_units_a, plan.cap_a), 128, 1, kSlotFwdUnits};
+    e = launch_lists(P, func, nfunc, &job, 1, H, s);
+    if (e != hipSuccess) return device_fail(e, "envelopes and unit list");
+    e = launch_mfma_fwd(q, k, v, o, P, job.U, H, func, nfunc, alpha, inv_max_len, s);
   } else {
     e = launch_generic_fwd(dtype, D, q, k, v, o, P, H, func, nfunc, alpha, inv_max_len, nullptr,
                            s);
@@ -303,26 +304,27 @@ extern "C" int hstu_attn_bwd(int dtype, const void* q, const void* k, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float inv_max_len = (float)(1.0 / (double)max_len);
   Prep P = prep_view(plan, workspace, (int)B, total);
-  hipError_t e = launch_prep(P, seq_offsets, target_rows, func, nfunc, s);
+  hipError_t e = launch_prep(P, seq_offsets, target_rows, s);
   if (e != hipSuccess) return device_fail(e, "prep");
   if (target_rows) {
     float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.off_partial);
-    Units U = units_view(workspace, plan.off_units_a, plan.cap_a);
-    e = launch_units(P, U, 128, 0, H, kSlotFwdUnits, s);
+    const UnitJob job{units_view(workspace, plan.off_units_a, plan.cap_a), 128, 0, kSlotFwdUnits};
+    e = launch_lists(P, nullptr, nfunc, &job, 1, H, s);
     if (e != hipSuccess) return device_fail(e, "unit list");
+    const Units& U = job.U;
     e = launch_targets_bwd(dtype, D, q, k, v, dout, dq, dk, dv, P, U, H, func, nfunc, alpha,
                            inv_max_len, target_rows, partial, s);
     if (e != hipSuccess) return device_fail(e, "targets-only backward");
     return HSTU_OK;
   }
   if (mfma_path(dtype, D)) {
-    Units Ukv = units_view(workspace, plan.off_units_b, plan.cap_b);
-    Units Uq = units_view(workspace, plan.off_units_c, plan.cap_c);
-    e = launch_units(P, Ukv, 128, 0, H, kSlotKvUnits, s);
-    if (e == hipSuccess) e = launch_units(P, Uq, 128, 1, H, kSlotQUnits, s);
-    if (e != hipSuccess) return device_fail(e, "unit list");
-    e = launch_mfma_bwd(q, k, v, dout, dq, dk, dv, P, Ukv, Uq, H, func, nfunc, alpha,
-                        inv_max_len, nullptr, 0, s);
+    const UnitJob jobs[2] = {
+        {units_view(workspace, plan.off_units_b, plan.cap_b), 128, 0, kSlotKvUnits},
+        {units_view(workspace, plan.off_units_c, plan.cap_c), 128, 1, kSlotQUnits}};
+    e = launch_lists(P, func, nfunc, jobs, 2, H, s);
+    if (e != hipSuccess) return device_fail(e, "envelopes and unit lists");
+    e = launch_mfma_bwd(q, k, v, dout, dq, dk, dv, P, jobs[0].U, jobs[1].U, H, func, nfunc,
+                        alpha, inv_max_len, nullptr, 0, s);
   } else {
     e = launch_generic_bwd(dtype, D, q, k, v, dout, dq, dk, dv, P, H, func, nfunc, alpha,
                            inv_max_len, nullptr, s);
@@ -382,7 +384,7 @@ int bwd_pstore_run(const Plan& plan, void* workspace, const void* q, const void*
   P.row_hi = row_hi;
   const int64_t rows = row_hi - row_lo;
   P.nrb_cap = (int)std::min<int64_t>(plan.nrb_cap, cdiv64(rows, kRB) + nb);
-  hipError_t e = launch_prep(P, seq_offsets, nullptr, func, nfunc, s);
+  hipError_t e = launch_prep(P, seq_offsets, nullptr, s);
   if (e != hipSuccess) return device_fail(e, "prep");
   // The size the lengths need is known on the device only; the kernels
   // compare it with pstore_bytes themselves (every P access is range-checked
@@ -391,13 +393,12 @@ int bwd_pstore_run(const Plan& plan, void* workspace, const void* q, const void*
   // hold, the sanitized lengths sum to `rows`, so the grids below hold
   // every unit.
   const int cap = std::min(plan.cap_b, round8((int64_t)H * (cdiv64(rows, 128) + nb)));
-  Units Ukv = units_view(workspace, plan.off_units_b, cap);
-  Units Uq = units_view(workspace, plan.off_units_c, cap);
-  e = launch_units(P, Ukv, 128, 0, H, kSlotKvUnits, s);
-  if (e == hipSuccess) e = launch_units(P, Uq, 128, 1, H, kSlotQUnits, s);
-  if (e != hipSuccess) return device_fail(e, "unit list");
-  e = launch_mfma_bwd(q, k, v, dout, dq, dk, dv, P, Ukv, Uq, H, func, nfunc, alpha, inv_max_len,
-                      static_cast<uint16_t*>(pstore), (uint64_t)pstore_bytes, s);
+  const UnitJob jobs[2] = {{units_view(workspace, plan.off_units_b, cap), 128, 0, kSlotKvUnits},
+                           {units_view(workspace, plan.off_units_c, cap), 128, 1, kSlotQUnits}};
+  e = launch_lists(P, func, nfunc, jobs, 2, H, s);
+  if (e != hipSuccess) return device_fail(e, "envelopes and unit lists");
+  e = launch_mfma_bwd(q, k, v, dout, dq, dk, dv, P, jobs[0].U, jobs[1].U, H, func, nfunc, alpha,
+                      inv_max_len, static_cast<uint16_t*>(pstore), (uint64_t)pstore_bytes, s);
   if (e != hipSuccess) return device_fail(e, "backward");
   return HSTU_OK;
 }
@@ -507,7 +508,7 @@ extern "C" int hstu_attn_check_inputs(const int64_t* seq_offsets, int64_t B, int
                 plan.bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   Prep P = prep_view(plan, workspace, (int)B, total);
-  hipError_t e = launch_prep(P, seq_offsets, target_rows, nullptr, 1, s);
+  hipError_t e = launch_prep(P, seq_offsets, target_rows, s);
   if (e != hipSuccess) return device_fail(e, "prep");
   int flags = 0;
   e = hipMemcpyAsync(&flags, P.flags, sizeof(int), hipMemcpyDeviceToHost, s);

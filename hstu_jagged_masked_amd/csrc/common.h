@@ -122,9 +122,17 @@ class ProfScope {
 // launchers (each returns a hipError_t from the launch)
 // ---------------------------------------------------------------------------
 hipError_t launch_prep(const Prep& P, const int64_t* seq_offsets, const int32_t* target_rows,
-                       const int32_t* func, int nfunc, hipStream_t stream);
-hipError_t launch_units(const Prep& P, const Units& U, int tile, int descending, int H,
-                        int count_slot, hipStream_t stream);
+                       hipStream_t stream);
+// One unit list to build: `U` for tiles of `tile` rows (descending: query
+// tiles, heaviest = highest index), its unit count stored in P.flags[count_slot].
+struct UnitJob {
+  Units U;
+  int tile, descending, count_slot;
+};
+// After launch_prep: the envelopes (when func is given; the MFMA kernels read
+// them) and up to two unit lists, in one launch.
+hipError_t launch_lists(const Prep& P, const int32_t* func, int nfunc, const UnitJob* jobs,
+                        int njobs, int H, hipStream_t stream);
 hipError_t launch_visible_counts(const int64_t* seq_offsets, int B, int64_t total,
                                  const int32_t* func, int nfunc, const int32_t* target_rows,
                                  int32_t* counts, int64_t* total_pairs, hipStream_t stream);

@@ -5,6 +5,8 @@
 // The interval semantics follow TorchEasyRec PR #670 ("What changed"):
 // interval 0 = [0, f0), interval j = [f(2j-1), f(2j)), empty when end <= start,
 // visible set = union, bounds sequence-local and clipped to [0, L).
+#include <algorithm>
+
 #include "common.h"
 #include "pstore.h"
 
@@ -249,14 +251,21 @@ __device__ __forceinline__ void put_record(int4* list, int64_t at, int4 a, int4 
 // heavy units start in the first round, spread over the XCDs.  (Units of
 // equal estimate take positions in an order the atomics decide; every unit
 // computes the same outputs wherever it runs.)
-__global__ __launch_bounds__(kUnitThreads) void k_units(Prep P, Units U, int tile,
-                                                        int descending, int H,
-                                                        int count_slot) {
-  __shared__ int hist[kSmallUnits];
-  __shared__ int part[kUnitThreads / 64];
-  __shared__ int smax;
+struct UnitShared {
+  int hist[kSmallUnits];
+  int part[kUnitThreads / 64];
+  int smax;
+};
+
+// Block `blk` of the list's grid (kUnitThreads threads).
+__device__ void units_block(const Prep& P, const UnitJob& J, int H, int blk, UnitShared& sh) {
+  const Units& U = J.U;
+  const int tile = J.tile, descending = J.descending, count_slot = J.count_slot;
+  int* const hist = sh.hist;
+  int* const part = sh.part;
+  int& smax = sh.smax;
   const int tid = threadIdx.x;
-  const int bid = blockIdx.x * blockDim.x + tid;
+  const int bid = blk * kUnitThreads + tid;
   const int* T = tile == 64 ? P.tiles64 : P.tiles128;
   const int B = P.B;
   const int n = H * T[B];
@@ -274,7 +283,7 @@ __global__ __launch_bounds__(kUnitThreads) void k_units(Prep P, Units U, int til
     return;
   }
   if (bid >= n && bid < U.cap) put_record(U.list, bid, idle_a, idle_c);
-  if (blockIdx.x != 0) return;
+  if (blk != 0) return;
   for (int i = tid; i < kSmallUnits; i += kUnitThreads) hist[i] = 0;
   if (tid == 0) smax = 0;
   // each thread's units, decoded once (their loads overlap)
@@ -337,17 +346,17 @@ __global__ __launch_bounds__(kUnitThreads) void k_units(Prep P, Units U, int til
   }
 }
 
-// One wave per row block: envelopes of every interval.
-__global__ __launch_bounds__(64) void k_envelopes(Prep P, const int32_t* __restrict__ func,
-                                                  int nfunc) {
-  const int g = blockIdx.x;
+// One wave per row block g: envelopes of every interval.
+__device__ void envelopes_wave(const Prep& P, const int32_t* __restrict__ func, int nfunc,
+                               int g) {
   const int nrb = P.rb_off[P.B];
   if (g >= nrb) return;
   const int b = upper_index(P.rb_off, P.B, g);
   const int rb = g - P.rb_off[b];
   const int64_t s = P.so[b];
   const int L = (int)(P.so[b + 1] - s);
-  const int i = rb * kRB + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int i = rb * kRB + lane;
   const bool valid = i < L;
   const int ni = (nfunc + 1) / 2;
   for (int j = 0; j < ni; ++j) {
@@ -361,8 +370,31 @@ __global__ __launch_bounds__(64) void k_envelopes(Prep P, const int32_t* __restr
       ilo = max(ilo, __shfl_xor(ilo, m, 64));
       ihi = min(ihi, __shfl_xor(ihi, m, 64));
     }
-    if (threadIdx.x == 0) P.env[(int64_t)g * ni + j] = make_int4(ulo, uhi, ilo, ihi);
+    if (lane == 0) P.env[(int64_t)g * ni + j] = make_int4(ulo, uhi, ilo, ihi);
   }
+}
+
+// What the kernels of one call need after k_prep, in one launch: blocks
+// [0, env_blocks) compute the envelopes (one wave per row block), then each
+// unit list takes its own run of blocks.  The parts are independent of each
+// other; all read only what k_prep wrote.
+constexpr int kEnvPerBlock = kUnitThreads / 64;
+
+__global__ __launch_bounds__(kUnitThreads) void k_lists(Prep P, const int32_t* __restrict__ func,
+                                                        int nfunc, int env_blocks, UnitJob J0,
+                                                        int blocks0, UnitJob J1, int H) {
+  __shared__ UnitShared sh;
+  int b = blockIdx.x;
+  if (b < env_blocks) {
+    envelopes_wave(P, func, nfunc, b * kEnvPerBlock + (threadIdx.x >> 6));
+    return;
+  }
+  b -= env_blocks;
+  if (b < blocks0) {
+    units_block(P, J0, H, b, sh);
+    return;
+  }
+  units_block(P, J1, H, b - blocks0, sh);
 }
 
 __global__ void k_zero_i64(int64_t* p) { *p = 0; }
@@ -416,28 +448,27 @@ __global__ void k_visible_counts(const int64_t* __restrict__ off, int B, int64_t
 }  // namespace
 
 hipError_t launch_prep(const Prep& P, const int64_t* seq_offsets, const int32_t* target_rows,
-                       const int32_t* func, int nfunc, hipStream_t stream) {
-  {
-    ProfScope ps(stream, "k_prep");
-    hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, stream, P, seq_offsets,
-                       target_rows);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || func == nullptr) return e;
-  if (P.nrb_cap > 0) {
-    ProfScope ps(stream, "k_envelopes");
-    hipLaunchKernelGGL(k_envelopes, dim3(P.nrb_cap), dim3(64), 0, stream, P, func, nfunc);
-    e = hipGetLastError();
-  }
-  return e;
+                       hipStream_t stream) {
+  ProfScope ps(stream, "k_prep");
+  hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, stream, P, seq_offsets,
+                     target_rows);
+  return hipGetLastError();
 }
 
-hipError_t launch_units(const Prep& P, const Units& U, int tile, int descending, int H,
-                        int count_slot, hipStream_t stream) {
-  const int blocks = (U.cap + kUnitThreads - 1) / kUnitThreads;
-  ProfScope ps(stream, "k_units");
-  hipLaunchKernelGGL(k_units, dim3(blocks > 0 ? blocks : 1), dim3(kUnitThreads), 0, stream, P, U,
-                     tile, descending, H, count_slot);
+hipError_t launch_lists(const Prep& P, const int32_t* func, int nfunc, const UnitJob* jobs,
+                        int njobs, int H, hipStream_t stream) {
+  const int env_blocks = func && P.nrb_cap > 0 ? (P.nrb_cap + kEnvPerBlock - 1) / kEnvPerBlock : 0;
+  UnitJob J[2] = {};
+  int blocks[2] = {0, 0};
+  for (int i = 0; i < njobs && i < 2; ++i) {
+    J[i] = jobs[i];
+    blocks[i] = std::max(1, (J[i].U.cap + kUnitThreads - 1) / kUnitThreads);
+  }
+  const int grid = env_blocks + blocks[0] + blocks[1];
+  if (grid == 0) return hipSuccess;
+  ProfScope ps(stream, "k_lists");
+  hipLaunchKernelGGL(k_lists, dim3(grid), dim3(kUnitThreads), 0, stream, P, func, nfunc,
+                     env_blocks, J[0], blocks[0], J[1], H);
   return hipGetLastError();
 }
 
