@@ -18,7 +18,9 @@
 //             separate lists); each block is one step (one LDS stage, one
 //             barrier), computed as two halves of 32 query rows:
 //               S = Q K^T, dS = dO V^T          (A from LDS, B = K, V registers)
-//               y, p in registers (mask via per-row bitmasks in LDS)
+//               y, p in registers (mask via per-row bitmasks in LDS, from
+//               the func columns of the block's rows, which a partly seen
+//               block's copy brings into LDS with its Q and dO tiles)
 //               dV^T += dO^T Y,  dK^T += Q^T P  (A = transpose reads of the
 //                                                row-major Q / dO tiles)
 //   k_bwd_q   one workgroup per (sequence, head, 128 query rows), the forward's
@@ -106,6 +108,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   __shared__ __attribute__((aligned(256))) uint16_t sQ0[kQStage], sQ1[kQStage];
   __shared__ __attribute__((aligned(256))) uint16_t sG0[kQStage], sG1[kQStage];  // dO
   __shared__ __attribute__((aligned(16))) uint32_t sMask[4][kStepRows];
+  // func columns of the step's rows (masked walks), copied with its tiles
+  __shared__ __attribute__((aligned(16))) int32_t sF0[kMaxNfunc][kStepRows],
+      sF1[kMaxNfunc][kStepRows];
   __shared__ int sPart[kStepWin], sFull[kStepWin];
   __shared__ int sCount[2];
 
@@ -116,7 +121,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   const int c0 = kt * kKvBN;
   const int c1 = min(c0 + kKvBN, L);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index in a scalar register: the copies' LDS addresses derive
+  // from it and stay scalar
+  const int wave = uniform(tid >> 6), lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
   const int ni = (nfunc + 1) / 2;
   const int64_t rs = (int64_t)H * kD;
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   int doff[kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < kDmaPerWave; ++i) doff[i] = swz_dma_offset((wave + 4 * i) * 64 + lane, rs2);
-  auto dma_step = [&](int q0, auto stage) {
+  auto dma_step = [&](int q0, auto stage, auto with_func) {
     constexpr int st = decltype(stage)::value;
     const int rows = min(kStepRows, L - q0);
     const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qh + (int64_t)q0 * rs, rows, rs2, kD * 2);
@@ -193,6 +200,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
       const int I = wave + 4 * i;
       lds_dma16(rq, (st ? sQ1 : sQ0) + I * 512, doff[i]);
       lds_dma16(rg, (st ? sG1 : sG0) + I * 512, doff[i]);
+    }
+    if constexpr (decltype(with_func)::value) {
+      // func column c of rows q0 + lane (rows past the sequence read 0),
+      // 4 bytes per lane; wave w copies columns w, w + 4, w + 8
+#pragma unroll
+      for (int i = 0; i < (kMaxNfunc + 3) / 4; ++i) {
+        const int c = wave + 4 * i;
+        if (c < nfunc) {
+          const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<int32_t*>(func + (int64_t)c * P.total + s), (short)0, L * 4, 0x00020000);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rf, (__attribute__((address_space(3))) void*)(st ? sF1[c] : sF0[c]), 4,
+              (q0 + lane) * 4, 0, 0, 0);
+        }
+      }
     }
   };
 
@@ -207,7 +229,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   const int rd_b0 = n * 256 + ((g ^ swz(n)) << 4);
   const int tr_b0 = trow * 256 + 8 * (gl & 1) +
                     ((((grp & 1) * 2 + ((gl & 3) >> 1)) ^ swz(trow)) << 4);
-  const int32_t* fseq = func + s;
 
   // one 64-row step (two halves of 32 rows) from LDS stage `stage`; `next`
   // (>= 0) is the next step's first row, whose DMA is issued after this
@@ -218,17 +239,31 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     const int nh = q0 + kKvBM < L ? 2 : 1;  // halves of 32 rows in this step
     if constexpr (kMasked) {
       // row q0 + 32 g + n (lane (n, g) takes one row of half g): visibility of
-      // this wave's 32 key columns (wave-private LDS), before the next step's
-      // copies so the func loads do not wait behind them
+      // this wave's 32 key columns (wave-private LDS), from the func columns
+      // copied with this step's tiles
+      const int rr = g * kKvBM + n, r = q0 + rr;
+      const int32_t(*sf)[kStepRows] = st ? sF1 : sF0;
       int lo[kMaxNI], hi[kMaxNI];
-      row_intervals_rsrc(fseq, P.total, q0 + g * kKvBM + n, ni, L, lo, hi);
-      sMask[wave][g * kKvBM + n] = col_mask32(lo, hi, ni, c0 + wave * 32);
+#pragma unroll
+      for (int j = 0; j < kMaxNI; ++j) {
+        lo[j] = L;
+        hi[j] = 0;
+        if (j < ni) {
+          const int a = j > 0 ? max(sf[2 * j - 1][rr], 0) : 0;
+          const int b = min(sf[2 * j][rr], L);
+          if (b > a && r < L) {
+            lo[j] = a;
+            hi[j] = b;
+          }
+        }
+      }
+      sMask[wave][rr] = col_mask32(lo, hi, ni, c0 + wave * 32);
     }
     if (next >= 0) {
       if constexpr (st == 0) {
-        dma_step(next, S1{});
+        dma_step(next, S1{}, masked);
       } else {
-        dma_step(next, S0{});
+        dma_step(next, S0{}, masked);
       }
     }
 #pragma unroll
@@ -302,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
 
   auto walk = [&](const int* list, int cnt, auto masked) {
     if (cnt == 0) return;
-    dma_step(list[0], S0{});
+    dma_step(list[0], S0{}, masked);
     for (int i = 0; i < cnt; i += 2) {
       dma_barrier();
       step(list[i], i + 1 < cnt ? list[i + 1] : -1, masked, S0{});
@@ -361,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
   const int64_t s = u.s;
   const int r0 = qt * kQBM;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = uniform(tid >> 6), lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
   const int ni = (nfunc + 1) / 2;
   const int64_t rs = (int64_t)H * kD;

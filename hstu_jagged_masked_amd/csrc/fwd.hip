@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
   const int64_t s = u.s;
   const int r0 = qt * kBM;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = uniform(tid >> 6), lane = tid & 63;
   const int n = lane & 31, g = lane >> 5;
   const int ni = (nfunc + 1) / 2;
   const int64_t rs = (int64_t)H * kD;  // row stride (elements)

@@ -134,40 +134,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 
-// Clipped intervals j < kMaxNI of local row r of a sequence of length L whose
-// func columns start at fseq (= func + first row of the sequence); empty
-// intervals, those with j >= ni, and every interval of a row r >= L come back
-// as lo = L, hi = 0.  Reads func through buffer resources so the only per-lane
-// state is the 32-bit offset r*4.
-__device__ __forceinline__ void row_intervals_rsrc(const int32_t* fseq, int64_t total, int r,
-                                                   int ni, int L, int* lo, int* hi) {
-  // every load is issued unconditionally (intervals j >= ni get an empty
-  // buffer, which reads zeros), so their latencies overlap
-  int a[kMaxNI], b[kMaxNI];
-#pragma unroll
-  for (int j = 0; j < kMaxNI; ++j) {
-    const bool on = j < ni;
-    const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int32_t*>(fseq + (on ? (int64_t)(2 * j) * total : 0)), (short)0,
-        on ? L * 4 : 0, 0x00020000);
-    b[j] = __builtin_amdgcn_raw_buffer_load_b32(re, r * 4, 0, 0);
-    a[j] = 0;
-    if (j > 0) {
-      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<int32_t*>(fseq + (on ? (int64_t)(2 * j - 1) * total : 0)), (short)0,
-          on ? L * 4 : 0, 0x00020000);
-      a[j] = __builtin_amdgcn_raw_buffer_load_b32(rl, r * 4, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxNI; ++j) {
-    const int x = max(a[j], 0), y = min(b[j], L);
-    const bool empty = y <= x || r >= L;
-    lo[j] = empty ? L : x;
-    hi[j] = empty ? 0 : y;
-  }
-}
-
 // Asynchronous 16-byte-per-lane copy from a buffer resource into LDS: lane l's
 // 16 bytes land at lds + 16*l (lds must be the same in every lane), whatever
 // global offset the lane reads; out-of-range lanes write zeros.  Completion is
