@@ -199,6 +199,17 @@ def test_bf16_random_func(hj, nfunc):
              seed=15)
 
 
+@pytest.mark.parametrize("path", ["default", "pstore", "targets"])
+def test_bf16_max_heads(hj, path):
+    """The largest head count the library accepts (255): row strides of
+    255 * 128 * 2 bytes, ragged lengths with partial tiles, a random mask."""
+    ls = np.array([130, 1, 257, 0, 64])
+    f = wl.func_random(ls, 5, 255, spread=12)
+    tr = wl.targets_last(ls) if path == "targets" else None
+    run_case(hj, ls, 255, 128, "bf16", f, 0.09, 257, seed=255, targets=tr,
+             pstore=path == "pstore")
+
+
 def test_bf16_targets_only(hj):
     ls = np.array([300, 1, 129, 700, 0, 64])
     tr = np.array([299, 0, 5, 699, 0, 63], dtype=np.int32)
