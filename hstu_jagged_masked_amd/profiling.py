@@ -103,9 +103,36 @@ def pmc(directories) -> str:
         if short not in KERNELS:
             continue
         out.append(f"== {short}")
-        for c, vals in sorted(counters.items()):
-            out.append(f"   {c:32s} {sum(vals) / len(vals):.6g}")
+        avg = {c: sum(vals) / len(vals) for c, vals in counters.items()}
+        for c in sorted(avg):
+            out.append(f"   {c:32s} {avg[c]:.6g}")
+        out.extend(derived(avg))
     return "\n".join(out)
+
+
+SIMDS = 1024  # 256 CUs x 4 SIMDs
+
+
+def derived(avg) -> list:
+    """Ratios of one kernel's counters (per-dispatch averages): VALU
+    instructions per MFMA instruction, the share of wave cycles spent waiting
+    for any instruction's inputs, the share of MFMA-busy cycles in which VALU
+    work co-executed, and MFMA-busy cycles per SIMD (divide by the kernel's
+    duration times the shader clock for the busy fraction)."""
+    out = []
+
+    def ratio(name, num, den):
+        if num in avg and den in avg and avg[den]:
+            out.append(f"   {name:32s} {avg[num] / avg[den]:.4g}")
+
+    ratio("VALU per MFMA instruction", "SQ_INSTS_VALU", "SQ_INSTS_MFMA")
+    ratio("wait cycles per wave cycle", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")
+    ratio("co-executed per MFMA-busy cycle", "SQ_VALU_MFMA_COEXEC_CYCLES",
+          "SQ_VALU_MFMA_BUSY_CYCLES")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        out.append(f"   {'MFMA-busy cycles per SIMD':32s} "
+                   f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / SIMDS:.4g}")
+    return out
 
 
 def _calibration(agg, counter):
