@@ -341,7 +341,9 @@ __device__ void units_block(const Prep& P, const UnitJob& J, int H, int blk, Uni
   for (int i = 0; i < kUnitsPerThread; ++i) {
     if (tid + i * kUnitThreads < n) {
       const int pos = atomicAdd(&hist[key[i]], 1);
-      put_record(U.list, pos, rec[i].a, rec[i].c);
+      // pos < n <= U.cap by the host's sizing of the list; the check keeps
+      // the write inside the list whatever the lengths
+      if (pos < U.cap) put_record(U.list, pos, rec[i].a, rec[i].c);
     }
   }
 }
