@@ -202,17 +202,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
       lds_dma16(rg, (st ? sG1 : sG0) + I * 512, doff[i]);
     }
     if constexpr (decltype(with_func)::value) {
-      // func column c of rows q0 + lane (rows past the sequence read 0),
-      // 4 bytes per lane; wave w copies columns w, w + 4, w + 8
+      // func column c of rows q0 + lane, 4 bytes per lane, through a
+      // resource over the step's rows (rows past the sequence read 0); wave
+      // w copies columns w, w + 4, w + 8
 #pragma unroll
       for (int i = 0; i < (kMaxNfunc + 3) / 4; ++i) {
         const int c = wave + 4 * i;
         if (c < nfunc) {
           const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(
-              const_cast<int32_t*>(func + (int64_t)c * P.total + s), (short)0, L * 4, 0x00020000);
+              const_cast<int32_t*>(func + (int64_t)c * P.total + s + q0), (short)0, rows * 4,
+              0x00020000);
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rf, (__attribute__((address_space(3))) void*)(st ? sF1[c] : sF0[c]), 4,
-              (q0 + lane) * 4, 0, 0, 0);
+              rf, (__attribute__((address_space(3))) void*)(st ? sF1[c] : sF0[c]), 4, lane * 4, 0,
+              0, 0);
         }
       }
     }
