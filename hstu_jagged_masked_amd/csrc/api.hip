@@ -66,8 +66,10 @@ bool plan_workspace(Plan& p, int is_bwd, int64_t B, int64_t total, int H, int D,
   p.off_t64 = take((size_t)(B + 1) * sizeof(int));
   p.off_t128 = take((size_t)(B + 1) * sizeof(int));
   p.off_env = take((size_t)nrb * p.ni * sizeof(int4));
-  // unit lists: tiles of 128 rows, H per tile
+  // unit lists: tiles of 128 rows, H per tile (one workgroup each: the
+  // count must fit a grid dimension)
   const int64_t cap128 = (int64_t)H * (cdiv64(total, 128) + B);
+  if (cap128 > INT32_MAX - kNumXcd) return false;
   p.cap_a = round8(cap128);
   p.cap_b = is_bwd ? round8(cap128) : 0;
   p.cap_c = is_bwd ? round8(cap128) : 0;

@@ -162,6 +162,18 @@ def test_bwd_pstore_rejects_bad_arguments(lib):
     assert call(ws_bytes=16) == -3
 
 
+def test_sizes_beyond_a_grid_are_refused(lib):
+    """H * (ceil(total/128) + B) workgroups must fit a launch grid: at the
+    largest H, B and total the plan is refused instead of overflowing."""
+    assert lib.hstu_attn_workspace_size(1, 1 << 24, (1 << 31) - 1, 255, 128, 5, 0) == 0
+    assert lib.hstu_attn_workspace_size(1, 1 << 24, (1 << 31) - 1, 1, 128, 5, 0) > 0
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    st = lib.hstu_attn_fwd(0, f, f, f, f, f, 1 << 24, (1 << 31) - 1, 255, 128, f, 5, 0.1, 8, None,
+                           f, 1 << 40, None)
+    assert st == -2 and "sizes out of range" in lib.hstu_last_error().decode()
+
+
 def test_bwd_pstore_chunked_rejects_bad_arguments(lib):
     """Malformed host offsets, and a buffer smaller than one sequence's stored
     P, are refused on the host before anything is enqueued (the library never
