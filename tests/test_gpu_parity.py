@@ -282,6 +282,28 @@ def test_stored_p_bitwise_repeatable(hj):
             assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("targets", [False, True])
+def test_autograd_wrapper_matches_entry_points(hj, targets):
+    """hstu_attention (torch.autograd.Function): the forward and the gradients
+    autograd hands back are bitwise those of attn_fwd / attn_bwd."""
+    ls = np.array([200, 0, 77, 131])
+    off = wl.offsets_from_lengths(ls)
+    off_t = torch.from_numpy(off).to(DEV)
+    f = torch.from_numpy(wl.func_sla(ls, 64, 16, 5)).to(DEV)
+    tr = torch.from_numpy(wl.targets_last(ls)).to(DEV) if targets else None
+    inp = make_inputs(ls, 2, 128, "bf16", 41, wl.targets_last(ls) if targets else None)
+    q, k, v, do = (inp[n][0] for n in ("q", "k", "v", "do"))
+    o_ref = hj.attn_fwd(q, k, v, off_t, f, 0.1, 200, tr)
+    g_ref = hj.attn_bwd(q, k, v, do, off_t, f, 0.1, 200, tr)
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o = hj.hstu_attention(qa, ka, va, off_t, f, 0.1, 200, tr)
+    o.backward(do)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o_ref)
+    for nm, got, want in zip(("dq", "dk", "dv"), (qa.grad, ka.grad, va.grad), g_ref):
+        assert torch.equal(got, want), nm
+
+
 def test_check_inputs(hj):
     off = torch.tensor([0, 3, 7], dtype=torch.int64, device=DEV)
     hj.check_inputs(off, 7)
