@@ -7,6 +7,8 @@ absolute bound alone would be weak).  The absolute bound is stated for outputs o
 unit scale; cases whose outputs exceed 1 in magnitude (a tiny max_len) apply it
 to err / max(1, max|ref|).  Visible counts are compared bit for bit.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -302,6 +304,67 @@ def test_autograd_wrapper_matches_entry_points(hj, targets):
     assert torch.equal(o.detach(), o_ref)
     for nm, got, want in zip(("dq", "dk", "dv"), (qa.grad, ka.grad, va.grad), g_ref):
         assert torch.equal(got, want), nm
+
+
+def random_case(seed):
+    """One random configuration: 1-8 sequences of 0-700 rows (empty, single-row
+    and every tail residue occur), 1-5 heads, a causal, SLA, three-interval or
+    arbitrary-bounds mask with nfunc 1-9, random alpha and max_len, and one of
+    the paths (default, stored P, stored P in runs over a small buffer,
+    targets-only with random candidates)."""
+    rng = np.random.Generator(np.random.PCG64(1000 + seed))
+    B = int(rng.integers(1, 9))
+    ls = rng.integers(0, 701, size=B)
+    ls[rng.random(B) < 0.15] = 0
+    ls[rng.random(B) < 0.1] = 1
+    H = int(rng.integers(1, 6))
+    kind = ["causal", "sla", "three", "random"][int(rng.integers(0, 4))]
+    if kind == "random":
+        nfunc = int(rng.choice([1, 3, 5, 7, 9]))
+    else:
+        nfunc = int(rng.choice([5, 9] if kind == "three" else [3, 5, 9]))
+    if kind == "causal":
+        f = wl.func_causal(ls, nfunc)
+    elif kind == "sla":
+        f = wl.func_sla(ls, int(rng.integers(1, 400)), int(rng.integers(0, 64)), nfunc)
+    elif kind == "three":
+        f = wl.func_three_interval(ls, int(rng.integers(1, 40)), int(rng.integers(1, 12)), nfunc)
+    else:
+        f = wl.func_random(ls, nfunc, 2000 + seed, spread=int(rng.integers(1, 40)))
+    alpha = float(rng.uniform(0.02, 0.3))
+    max_len = int(max(1, ls.max()) * rng.uniform(0.5, 2.0)) + 1
+    path = ["default", "pstore", "runs", "targets"][int(rng.integers(0, 4))]
+    tr = None
+    if path == "targets":
+        tr = np.array([int(rng.integers(0, L)) if L > 0 else 0 for L in ls], np.int32)
+    return ls, H, f, alpha, max_len, path, tr
+
+
+SWEEP_CASES = int(os.environ.get("HSTU_SWEEP_CASES", "12"))
+
+
+@pytest.mark.parametrize("seed", range(SWEEP_CASES))
+def test_random_sweep(hj, seed):
+    """Random configurations against the oracle (HSTU_SWEEP_CASES sets how
+    many); the stored-P runs path must also reproduce the whole-buffer one
+    bitwise."""
+    ls, H, f, alpha, max_len, path, tr = random_case(seed)
+    print(f"seed {seed}: lengths {ls.tolist()} H {H} nfunc {f.shape[0]} path {path}", flush=True)
+    run_case(hj, ls, H, 128, "bf16", f, alpha, max_len, seed=3000 + seed, targets=tr,
+             pstore=path in ("pstore", "runs"))
+    if path == "runs":
+        off = wl.offsets_from_lengths(ls)
+        off_t = torch.from_numpy(off).to(DEV)
+        inp = make_inputs(ls, H, 128, "bf16", 3000 + seed)
+        args = (inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], off_t,
+                torch.from_numpy(np.ascontiguousarray(f)).to(DEV), alpha, max_len)
+        ref = hj.attn_bwd(*args, pstore=pstore_for(hj, off_t, H))
+        per_seq = max(-(-int(L) // 128) * -(-int(L) // 32) * 8192 * H for L in ls)
+        buf = torch.empty(max(per_seq, 256), dtype=torch.uint8, device=DEV)
+        got = hj.attn_bwd(*args, pstore=buf, host_offsets=torch.from_numpy(off))
+        torch.cuda.synchronize()
+        for a, b, nm in zip(ref, got, ("dq", "dk", "dv")):
+            assert torch.equal(a, b), f"runs path {nm} differs"
 
 
 def test_check_inputs(hj):
