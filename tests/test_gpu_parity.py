@@ -367,6 +367,27 @@ def test_random_sweep(hj, seed):
             assert torch.equal(a, b), f"runs path {nm} differs"
 
 
+@pytest.mark.parametrize("seed", range(max(4, SWEEP_CASES // 2)))
+def test_random_sweep_generic(hj, seed):
+    """The plain-FMA kernels (fp32 at D = 32, 64, 128; bf16 at D = 32, 64) on
+    random configurations against the oracle, full-length and targets-only."""
+    ls, H, f, alpha, max_len, path, tr = random_case(10000 + seed)
+    rng = np.random.Generator(np.random.PCG64(20000 + seed))
+    dtype, D = [("fp32", 32), ("fp32", 64), ("fp32", 128), ("bf16", 32), ("bf16", 64)][
+        int(rng.integers(0, 5))]
+    ls = np.minimum(ls, 300)  # the plain kernels are slow; keep the case small
+    f = random_case_func(ls, f.shape[0], seed)
+    tr = None if path != "targets" else np.array(
+        [int(rng.integers(0, L)) if L > 0 else 0 for L in ls], np.int32)
+    print(f"seed {seed}: {dtype} D {D} lengths {ls.tolist()} H {H} targets {tr is not None}",
+          flush=True)
+    run_case(hj, ls, H, D, dtype, f, alpha, max_len, seed=4000 + seed, targets=tr)
+
+
+def random_case_func(ls, nfunc, seed):
+    return wl.func_random(ls, nfunc, 5000 + seed, spread=12)
+
+
 def test_check_inputs(hj):
     off = torch.tensor([0, 3, 7], dtype=torch.int64, device=DEV)
     hj.check_inputs(off, 7)
