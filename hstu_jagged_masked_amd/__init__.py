@@ -291,21 +291,31 @@ def profile_read() -> dict:
 
 class HstuAttention(torch.autograd.Function):
     """Autograd wrapper: forward = attn_fwd, backward = attn_bwd (nothing saved
-    but the inputs: HSTU attention has no softmax statistics to keep)."""
+    but the inputs: HSTU attention has no softmax statistics to keep).  With
+    ``pstore`` (and optionally ``host_offsets``) the backward is the stored-P
+    one, as in attn_bwd."""
 
     @staticmethod
-    def forward(ctx, q, k, v, seq_offsets, func, alpha, max_len, target_rows):
+    def forward(ctx, q, k, v, seq_offsets, func, alpha, max_len, target_rows, pstore,
+                host_offsets):
         ctx.save_for_backward(q, k, v, seq_offsets, func, target_rows)
         ctx.alpha, ctx.max_len = alpha, max_len
+        ctx.pstore, ctx.host_offsets = pstore, host_offsets
         return attn_fwd(q, k, v, seq_offsets, func, alpha, max_len, target_rows)
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v, seq_offsets, func, target_rows = ctx.saved_tensors
         dq, dk, dv = attn_bwd(q, k, v, dout.contiguous(), seq_offsets, func, ctx.alpha,
-                              ctx.max_len, target_rows)
-        return dq, dk, dv, None, None, None, None, None
+                              ctx.max_len, target_rows, pstore=ctx.pstore,
+                              host_offsets=ctx.host_offsets)
+        return dq, dk, dv, None, None, None, None, None, None, None
 
 
-def hstu_attention(q, k, v, seq_offsets, func, alpha, max_len, target_rows=None):
-    return HstuAttention.apply(q, k, v, seq_offsets, func, alpha, max_len, target_rows)
+def hstu_attention(q, k, v, seq_offsets, func, alpha, max_len, target_rows=None, pstore=None,
+                   host_offsets=None):
+    """HSTU attention with autograd.  ``pstore``: a uint8 CUDA buffer for the
+    stored-P backward (bf16, D = 128, full-length), of pstore_bytes() bytes,
+    or smaller when ``host_offsets`` (a CPU copy of seq_offsets) is given."""
+    return HstuAttention.apply(q, k, v, seq_offsets, func, alpha, max_len, target_rows, pstore,
+                               host_offsets)

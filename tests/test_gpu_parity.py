@@ -304,6 +304,20 @@ def test_autograd_wrapper_matches_entry_points(hj, targets):
     assert torch.equal(o.detach(), o_ref)
     for nm, got, want in zip(("dq", "dk", "dv"), (qa.grad, ka.grad, va.grad), g_ref):
         assert torch.equal(got, want), nm
+    if targets:
+        return
+    # the stored-P backward through autograd, over a whole-batch and a small buffer
+    ps = pstore_for(hj, off_t, 2)
+    g_p = hj.attn_bwd(q, k, v, do, off_t, f, 0.1, 200, pstore=ps)
+    small = torch.empty(max(-(-int(L) // 128) * -(-int(L) // 32) * 8192 * 2 for L in ls),
+                        dtype=torch.uint8, device=DEV)
+    for buf, host in ((ps, None), (small, torch.from_numpy(off))):
+        qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+        hj.hstu_attention(qa, ka, va, off_t, f, 0.1, 200, pstore=buf,
+                          host_offsets=host).backward(do)
+        torch.cuda.synchronize()
+        for nm, got, want in zip(("dq", "dk", "dv"), (qa.grad, ka.grad, va.grad), g_p):
+            assert torch.equal(got, want), "stored-P " + nm
 
 
 def random_case(seed):
