@@ -298,10 +298,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
           // silu'(alpha x) = sg + alpha * x sg (1 - sg) = sg + alpha * (y - y sg)
           float p = dsacc[r] * fmaf(alpha, fmaf(-y, sg, y), sg);
           if constexpr (kMasked) {
-            if (!((mrow[i] >> n) & 1u)) {
-              y = 0.f;
-              p = 0.f;
-            }
+            const uint32_t keep = bit_keep(mrow[i], n);
+            y = keep_bits(y, keep);
+            p = keep_bits(p, keep);
           }
           yb[r >> 3][r & 7] = (__bf16)y;
           pb[r >> 3][r & 7] = (__bf16)p;
@@ -512,10 +511,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_q(
         // silu'(alpha x) = sg + alpha * x sg (1 - sg)
         const float y = x * sg;
         float p = dsacc[kb][r] * fmaf(alpha, fmaf(-y, sg, y), sg);
-        if constexpr (kMasked) {
-          const int bit = (r >> 2) * 8 + (r & 3);
-          if (!((mg >> bit) & 1u)) p = 0.f;
-        }
+        if constexpr (kMasked) p = keep_bits(p, bit_keep_imm(mg, (r >> 2) * 8 + (r & 3)));
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
     }

@@ -304,4 +304,22 @@ __device__ __forceinline__ float logistic_scaled(float x, float c) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(c * x));
 }
 
+// x where bit b of m is set, +0 where it is clear.  The signed one-bit field
+// extract is all ones or all zeros, and it is and-ed with the float's bits: two
+// instructions per element, with no compare, select or separate conversion.
+// bit_keep takes a per-lane b; bit_keep_imm a b that is a constant after
+// unrolling (inline assembly: the compiler turns a field extract at a known
+// offset back into a compare and a select).
+__device__ __forceinline__ uint32_t bit_keep(uint32_t m, int b) {
+  return (uint32_t)__builtin_amdgcn_sbfe((int)m, b, 1);
+}
+__device__ __forceinline__ uint32_t bit_keep_imm(uint32_t m, int b) {
+  uint32_t k;
+  asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(k) : "v"(m), "I"(b));
+  return k;
+}
+__device__ __forceinline__ float keep_bits(float x, uint32_t keep) {
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) & keep);
+}
+
 }  // namespace hstu

@@ -156,10 +156,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(
       for (int r = 0; r < 16; ++r) {
         const float x = sacc[kb][r];
         float y = x * logistic_scaled(x, c_exp);
-        if constexpr (kMasked) {
-          const int bit = (r >> 2) * 8 + (r & 3);
-          if (!((mg >> bit) & 1u)) y = 0.f;
-        }
+        if constexpr (kMasked) y = keep_bits(y, bit_keep_imm(mg, (r >> 2) * 8 + (r & 3)));
         pf[kb * 2 + (r >> 3)][r & 7] = (__bf16)y;
       }
     }
