@@ -3,11 +3,18 @@
     python -m hstu_jagged_masked_amd.profiling stats DIR          # --kernel-trace --stats CSVs
     python -m hstu_jagged_masked_amd.profiling pmc DIR [DIR ...]  # --pmc counter CSVs
     python -m hstu_jagged_masked_amd.profiling traffic FETCH_DIR WRITE_DIR OUT.json
+    python -m hstu_jagged_masked_amd.profiling isa                # compiled hot loops
 
 ``stats`` prints per-kernel launch count and average / total duration.
 ``pmc`` prints the average of each counter per dispatch, per kernel.
 ``traffic`` turns FETCH_SIZE and WRITE_SIZE (KiB per dispatch) into HBM bytes per
-launch of each MFMA/streaming kernel.  The raw counters are scaled by the
+launch of each MFMA/streaming kernel.
+``isa`` compiles the MFMA kernels' sources to gfx950 assembly (the library's
+own flags) and prints the instruction mix of each basic block that issues
+at least 16 MFMAs (the tile and step bodies): MFMAs, transcendentals, other
+VALU instructions, LDS reads, and, where the block evaluates SiLU (two
+transcendentals per score element), those counts per 64 score elements, i.e.
+per accumulator register.  The raw counters are scaled by the
 factor that maps the same counter of a plain device-to-device copy of known
 size (the ``bench.py`` calibration copy, a device-to-device hipMemcpy that the
 runtime performs with its copy kernel; the largest such dispatch in the run)
@@ -173,11 +180,81 @@ def traffic(fetch_dir: str, write_dir: str, out_path: str, copy_bytes: int) -> d
     return result
 
 
+ISA_SOURCES = ("fwd.hip", "bwd.hip", "dq.hip")
+TRANSCENDENTAL = ("v_exp_f32", "v_rcp_f32")
+
+
+def isa_blocks(asm_text: str):
+    """[(kernel, block, Counter of opcodes)] over the blocks of each kernel."""
+    out, kernel, block, ops = [], None, None, None
+    for line in asm_text.splitlines():
+        t = line.strip()
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            kernel, block, ops = short_name_isa(m.group(1)), "entry", collections.Counter()
+            out.append((kernel, block, ops))
+            continue
+        if kernel is None or not t or t.startswith(";"):
+            continue
+        if t.startswith(".Lfunc_end"):
+            kernel = None
+            continue
+        m = re.match(r"^(\.LBB\w+):", t)
+        if m:
+            block, ops = m.group(1), collections.Counter()
+            out.append((kernel, block, ops))
+            continue
+        if t.startswith("."):
+            continue
+        ops[t.split()[0]] += 1
+    return out
+
+
+def short_name_isa(symbol: str) -> str:
+    m = re.search(r"(k_\w+?)(I[LbB0-9E]+)?E", symbol)
+    name = m.group(1) if m else symbol[:40]
+    if name == "k_bwd_kv" and "ILb1E" in symbol:
+        name = "k_bwd_kv_p"
+    return name
+
+
+def isa(build_dir: str = None) -> str:
+    import subprocess
+    from . import build as bld
+    build_dir = build_dir or bld.BUILD
+    os.makedirs(build_dir, exist_ok=True)
+    flags = [f for f in bld.COMPILE_FLAGS if not f.startswith("-Rpass")]
+    lines = ["kernel        block       mfma trans valu  lds_rd | per 64 elements: valu trans "
+             "(valu = other vector ALU instructions)"]
+    for src in ISA_SOURCES:
+        out = os.path.join(build_dir, src + ".s")
+        cmd = [bld.HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(PKG, "csrc", src),
+               "-o", out]
+        proc = subprocess.run(cmd, capture_output=True, text=True)
+        if proc.returncode != 0:
+            raise RuntimeError(f"hipcc -S failed for {src}:\n{proc.stderr}")
+        with open(out) as f:
+            for kernel, block, ops in isa_blocks(f.read()):
+                mfma = sum(v for k, v in ops.items() if k.startswith("v_mfma"))
+                if mfma < 16:
+                    continue
+                trans = sum(v for k, v in ops.items() if k.startswith(TRANSCENDENTAL))
+                valu = sum(v for k, v in ops.items() if k.startswith("v_") and
+                           not k.startswith(("v_mfma", "v_accvgpr") + TRANSCENDENTAL))
+                lds = sum(v for k, v in ops.items() if k.startswith("ds_read"))
+                per = (f"{valu / (trans / 2):6.2f} {2.0:5.1f}" if trans else "")
+                lines.append(f"{kernel:13s} {block:11s} {mfma:4d} {trans:5d} {valu:4d} {lds:6d}"
+                             f" | {per}")
+    return "\n".join(lines)
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "stats":
         print(stats(argv[1]))
     elif len(argv) >= 2 and argv[0] == "pmc":
         print(pmc(argv[1:]))
+    elif len(argv) >= 1 and argv[0] == "isa":
+        print(isa())
     elif len(argv) >= 4 and argv[0] == "traffic":
         copy_bytes = int(argv[4]) if len(argv) > 4 else 1 << 30
         print(json.dumps(traffic(argv[1], argv[2], argv[3], copy_bytes), indent=1))
