@@ -157,6 +157,40 @@ def split_ms(hj, torch, t, cfg, steps, pstore):
     return out
 
 
+def dq_variants(hj, torch, t, cfg, steps, stored_p_bwd_ms):
+    """The backward alone with each dQ path on the same inputs: stored P (its
+    time from split_ms), recompute (a query-owner pass that recomputes the
+    scores) and atomic (fp32 atomics from the key-owner pass; dq not bitwise
+    repeatable).  ms per backward and per-kernel ms."""
+    acc = torch.empty(t["k"].shape, dtype=torch.float32, device=t["k"].device)
+    a = (t["q"], t["k"], t["v"], t["do"], t["off"], t["func"], cfg["alpha"], cfg["max_len"])
+    calls = {"recompute": lambda: hj.attn_bwd(*a),
+             "atomic": lambda: hj.attn_bwd_atomic(*a, dq_accum=acc)}
+    out = {"stored_p": {"bwd_ms": stored_p_bwd_ms}}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        hj.profile_reset()
+        hj.profile_enable(True)
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        hj.profile_enable(False)
+        prof = hj.profile_read()
+        out[name] = {"bwd_ms": round(e0.elapsed_time(e1) / steps, 4),
+                     "kernels_ms": {k: round(v[1] / steps, 4) for k, v in sorted(prof.items())}}
+    del acc
+    torch.cuda.empty_cache()
+    return out
+
+
 def step_stats(hj, torch, t, cfg, steps, runs, pstore):
     """Per-step fwd+bwd times (a HIP event pair around each step), `runs`
     runs of `steps` steps after the timed region: median and min of each run
@@ -363,6 +397,8 @@ def main():
     ap.add_argument("--pstore-budget-gb", type=float, default=4.0,
                     help="also time the stored-P backward over a buffer of this many GiB, in "
                          "runs of sequences (0: skip)")
+    ap.add_argument("--no-dq-variants", dest="dq_variants", action="store_false",
+                    help="skip timing the backward with the recompute and atomic dQ paths")
     ap.add_argument("--no-extra", dest="extra", action="store_false",
                     help="skip the other workloads (SLA, three-interval, OneRank, ragged, "
                          "L=4086) and the full CPU record")
@@ -485,6 +521,12 @@ def main():
     del t3
     log(f"[bench] sla_2k nfunc 3 vs 5: {pad}")
 
+    variants = None
+    if args.dq_variants:
+        variants = dq_variants(hj, torch, t, cfg, min(args.steps, 5), split["bwd"])
+        log(f"[bench] backward by dQ path: " +
+            ", ".join(f"{k} {v['bwd_ms']} ms" for k, v in variants.items()))
+
     cpu = None
     if args.cpu_seqs > 0:
         log(f"[bench] cpu oracle baseline on {args.cpu_seqs} sequences ...")
@@ -534,6 +576,7 @@ def main():
         "cpu_baseline": cpu,
         "targets_only": targets,
         "pstore_bounded": chunked,
+        "dq_variants": variants,
         "nfunc_pad_cost": pad,
         "per_workload": per_workload,
         "kernels": kernels,

@@ -82,6 +82,9 @@ def library() -> ctypes.CDLL:
     lib.hstu_attn_bwd_pstore_chunked.argtypes = [P, P, P, P, P, P, P, P, P, i64, i64, i32, i32, P,
                                                  i32, f32, i64, P, sz, P, sz, P]
     lib.hstu_attn_bwd_pstore_chunked.restype = i32
+    lib.hstu_attn_bwd_atomic.argtypes = [P, P, P, P, P, P, P, P, i64, i64, i32, i32, P, i32, f32,
+                                         i64, P, sz, P, sz, P]
+    lib.hstu_attn_bwd_atomic.restype = i32
     lib.hstu_attn_pstore_bytes.argtypes = [P, i64, i64, i32]
     lib.hstu_attn_pstore_bytes.restype = sz
     lib.hstu_profile_enable.argtypes = [i32]
@@ -96,6 +99,7 @@ def library() -> ctypes.CDLL:
 
 EXPORTED = ("hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size", "hstu_attn_fwd",
             "hstu_attn_fwd_noalloc", "hstu_attn_bwd", "hstu_attn_bwd_pstore", "hstu_attn_bwd_pstore_chunked",
+            "hstu_attn_bwd_atomic",
             "hstu_attn_pstore_bytes",
             "hstu_attn_visible_counts", "hstu_attn_check_inputs",
             "hstu_profile_enable", "hstu_profile_read", "hstu_profile_reset")
@@ -243,6 +247,34 @@ def attn_bwd(q, k, v, dout, seq_offsets, func, alpha, max_len, target_rows=None,
         code, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(seq_offsets), B, total, H, D, _ptr(func), nfunc, float(alpha), int(max_len),
         _ptr(target_rows), _ptr(ws), ws.numel(), _stream(k.device)))
+    return dq, dk, dv
+
+
+def attn_bwd_atomic(q, k, v, dout, seq_offsets, func, alpha, max_len, dq_accum=None):
+    """Backward with dQ accumulated by fp32 atomics in the key-owner pass
+    (bf16, D = 128, full-length mode): dk and dv as attn_bwd (bitwise), dq up
+    to the order of its fp32 additions (not bitwise repeatable).  ``dq_accum``
+    is an optional float32 CUDA tensor of at least total*H*D elements used as
+    the accumulator (allocated here when not given)."""
+    B, total, H, D, nfunc = _common(q, k, seq_offsets, func, None)
+    for t in (q, k, v, dout):
+        if not t.is_contiguous() or t.dtype != k.dtype:
+            raise ValueError("q, k, v, dout must be contiguous and share a dtype")
+    if _dtype_code(k) != HSTU_BF16:
+        raise ValueError("the atomic-dQ backward needs bf16")
+    if dq_accum is None:
+        dq_accum = torch.empty((total, H, D), dtype=torch.float32, device=k.device)
+    if dq_accum.dtype != torch.float32 or not dq_accum.is_contiguous():
+        raise ValueError("dq_accum must be a contiguous float32 tensor")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws_bytes = workspace_size(1, B, total, H, D, nfunc, False)
+    ws = _workspace(ws_bytes, k.device)
+    _check(library().hstu_attn_bwd_atomic(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(seq_offsets), B, total, H, D, _ptr(func), nfunc, float(alpha), int(max_len),
+        _ptr(ws), ws.numel(), _ptr(dq_accum), dq_accum.numel() * 4, _stream(k.device)))
     return dq, dk, dv
 
 

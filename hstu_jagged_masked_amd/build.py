@@ -37,11 +37,13 @@ COMPILE_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-# kernels whose resources are checked: (minimum waves per SIMD, maximum scratch
-# bytes per lane).  A few bytes of scratch are spills of values used outside
+# kernels whose resources are checked (by mangled-name fragment; the key-owner
+# kernel's instantiations <store P, atomic dQ> separately): (minimum waves per
+# SIMD, maximum scratch bytes per lane).  The atomic-dQ instantiation runs one
+# wave per SIMD by design.  A few bytes of scratch are spills of values used outside
 # the tile loops; hundreds mean a register array was demoted to memory.
-HOT_KERNELS = {"k_fwd_bf16": (2, 64), "k_bwd_kv": (2, 192), "k_bwd_q": (2, 64),
-               "k_bwd_dq": (2, 64)}
+HOT_KERNELS = {"k_fwd_bf16": (2, 64), "k_bwd_kvILb0ELb0E": (2, 192), "k_bwd_kvILb1ELb0E": (2, 192),
+               "k_bwd_kvILb0ELb1E": (1, 64), "k_bwd_q": (2, 64), "k_bwd_dq": (2, 64)}
 
 
 def _resource_report(stderr: str):

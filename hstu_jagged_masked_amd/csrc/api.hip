@@ -474,6 +474,44 @@ extern "C" int hstu_attn_bwd_pstore_chunked(const void* q, const void* k, const 
   return HSTU_OK;
 }
 
+extern "C" int hstu_attn_bwd_atomic(const void* q, const void* k, const void* v, const void* dout,
+                                    void* dq, void* dk, void* dv, const int64_t* seq_offsets,
+                                    int64_t B, int64_t total, int H, int D, const int32_t* func,
+                                    int nfunc, float alpha, int64_t max_len, void* workspace,
+                                    size_t workspace_bytes, void* dq_accum, size_t dq_accum_bytes,
+                                    void* stream) {
+  Plan plan;
+  int st = validate(plan, 1, HSTU_BF16, B, total, H, D, nfunc, alpha, max_len, seq_offsets, func,
+                    nullptr, workspace, workspace_bytes);
+  if (st) return st;
+  if (D != 128)
+    return fail(HSTU_ERR_UNSUPPORTED, "the atomic-dQ backward needs D = 128, got %d", D);
+  if ((st = check_tensor(q, total, "q")) || (st = check_tensor(k, total, "k")) ||
+      (st = check_tensor(v, total, "v")) || (st = check_tensor(dout, total, "dout")) ||
+      (st = check_tensor(dq, total, "dq")) || (st = check_tensor(dk, total, "dk")) ||
+      (st = check_tensor(dv, total, "dv")))
+    return st;
+  const uint64_t need = (uint64_t)total * (uint64_t)H * (uint64_t)D * 4u;
+  if (total > 0 && !dq_accum) return fail(HSTU_ERR_INVALID, "dq_accum is NULL");
+  if (reinterpret_cast<uintptr_t>(dq_accum) & 255u)
+    return fail(HSTU_ERR_INVALID, "dq_accum must be 256-byte aligned");
+  if ((uint64_t)dq_accum_bytes < need)
+    return fail(HSTU_ERR_INVALID, "dq_accum holds %zu bytes; [total, H, D] fp32 needs %llu",
+                dq_accum_bytes, (unsigned long long)need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Prep P = prep_view(plan, workspace, (int)B, total);
+  hipError_t e = launch_prep(P, seq_offsets, nullptr, s);
+  if (e != hipSuccess) return device_fail(e, "prep");
+  const UnitJob job{units_view(workspace, plan.off_units_b, plan.cap_b), 128, 0, kSlotKvUnits};
+  e = launch_lists(P, func, nfunc, &job, 1, H, s);
+  if (e != hipSuccess) return device_fail(e, "envelopes and unit list");
+  e = launch_mfma_bwd_atomic(q, k, v, dout, dq, dk, dv, P, job.U, H, func, nfunc, alpha,
+                             (float)(1.0 / (double)max_len), static_cast<float*>(dq_accum), total,
+                             s);
+  if (e != hipSuccess) return device_fail(e, "atomic-dQ backward");
+  return HSTU_OK;
+}
+
 extern "C" int hstu_attn_visible_counts(const int64_t* seq_offsets, int64_t B, int64_t total,
                                         const int32_t* func, int nfunc,
                                         const int32_t* target_rows, int32_t* counts,

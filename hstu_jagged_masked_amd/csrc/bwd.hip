@@ -31,6 +31,12 @@
 // Both stage their tiles in LDS with asynchronous buffer-to-LDS DMA into two
 // stages: the next step's copy runs during this step's math, and the one
 // barrier per step both publishes the copy and retires the other stage.
+//
+// The atomic-dQ variant (k_bwd_kv<false, true>) replaces k_bwd_q: after each
+// half the four waves exchange their bf16 P through LDS, wave w forms
+// dQ[32 rows][dims 32w..32w+31] = P[32 rows][128 keys] K[128 keys][those dims]
+// with K from registers, and adds it to an fp32 accumulator with global
+// atomics (in no fixed order: dq is not bitwise repeatable).
 #include <type_traits>
 
 #include "common.h"
@@ -96,13 +102,18 @@ __device__ __forceinline__ void step_window(const int4* env, int ni, int L, int 
 // P is formed (holding the second half's until after the next barrier
 // measured the same).  Only the halves a key tile walks are written; the dQ
 // pass reads exactly those.
-template <bool kStoreP>
-__global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
+//
+// kAtomicDQ: also add each half's dQ contribution to dq_acc (fp32 [total, H,
+// D]) with atomics, as described at the top.  The exchange buffers and the
+// K operands of the dQ product do not fit beside two workgroups per CU, so
+// this instantiation runs one workgroup (one wave per SIMD) per CU.
+template <bool kStoreP, bool kAtomicDQ>
+__global__ __launch_bounds__(kThreads, kAtomicDQ ? 1 : 2) void k_bwd_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, Prep P, const int4* __restrict__ units, int H,
     const int32_t* __restrict__ func, int nfunc, float alpha, float out_scale,
-    uint16_t* __restrict__ pstore, uint64_t pstore_cap) {
+    uint16_t* __restrict__ pstore, uint64_t pstore_cap, float* __restrict__ dq_acc) {
   // two LDS stages as separate objects, so the compiler sees that the DMA
   // filling one stage does not alias the reads of the other
   __shared__ __attribute__((aligned(256))) uint16_t sQ0[kQStage], sQ1[kQStage];
@@ -113,6 +124,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
       sF1[kMaxNfunc][kStepRows];
   __shared__ int sPart[kStepWin], sFull[kStepWin];
   __shared__ int sCount[2];
+  // atomic dQ: per half, the four waves' P registers (2 KiB each)
+  __shared__ __attribute__((aligned(16))) uint16_t sX[kAtomicDQ ? 2 * 4 * 1024 : 8];
 
   UnitRec u;
   if (!unit_of_block(units, u)) return;
@@ -156,6 +169,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
     for (int ks = 0; ks < kD / 16; ++ks) {
       kf[ks] = col_ok ? *reinterpret_cast<const bf16x8*>(kp + ks * 16) : bf16x8{};
       vf[ks] = col_ok ? *reinterpret_cast<const bf16x8*>(vp + ks * 16) : bf16x8{};
+    }
+  }
+  // atomic dQ: B operands of dQ[rows][dims] += P K, this wave's 32 dims
+  // (32 wave + n) and the tile's 128 keys: lane (n, g) holds keys
+  // 16 ks + 8 g + 0..7 (zero past the sequence end)
+  bf16x8 kq[kAtomicDQ ? kKvBN / 16 : 1];
+  if constexpr (kAtomicDQ) {
+    const uint16_t* kd = k + s * rs + (int64_t)h * kD + wave * 32 + n;
+#pragma unroll
+    for (int ks = 0; ks < kKvBN / 16; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = c0 + 16 * ks + 8 * g + e;
+        const uint16_t bits = key < L ? kd[(int64_t)key * rs] : (uint16_t)0;
+        kq[ks][e] = __builtin_bit_cast(__bf16, bits);
+      }
     }
   }
   f32x16 dkacc[kD / 32], dvacc[kD / 32];
@@ -232,6 +261,41 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
   const int tr_b0 = trow * 256 + 8 * (gl & 1) +
                     ((((grp & 1) * 2 + ((gl & 3) >> 1)) ^ swz(trow)) << 4);
 
+  // Atomic dQ of one half (query rows from r0h): each wave writes its P
+  // registers to the half's exchange buffer (2 KiB per wave: key rows of 64
+  // bytes, the 16-byte chunk of lane (n, g) at g ^ ((n/4) mod 4)), and reads
+  // the tile's 128 keys back with transpose reads, so that lane l holds keys
+  // 16 ks + 8 (l/32) + 0..7 of row position l % 32: the A operand of
+  // dQ[row position][dim] += P K.  Row position hh*16 + g'*8 + e is query row
+  // (2 hh + e/4)*8 + g'*4 + e%4 of the half (the order of the P registers).
+  // The two halves use separate buffers; the barrier before each step
+  // retires a buffer before the next step rewrites it.
+  const int pw_b0 = n * 64 + ((g ^ ((n >> 2) & 3)) << 4);
+  const int pr_b0 = (8 * (grp >> 1) + (gl >> 2)) * 64 +
+                    ((((grp & 1) * 2 + ((gl & 3) >> 1)) ^ (2 * (grp >> 1))) << 4) +
+                    (gl & 1) * 8;
+  auto dq_atomic = [&](int r0h, int hf, const bf16x8* pv) {
+    char* xb = reinterpret_cast<char*>(sX) + hf * 8192;
+    *reinterpret_cast<bf16x8*>(xb + wave * 2048 + pw_b0) = pv[0];
+    *reinterpret_cast<bf16x8*>(xb + wave * 2048 + (pw_b0 ^ 32)) = pv[1];
+    lds_barrier();
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < kKvBN / 16; ++ks) {
+      const uint16_t* rb = reinterpret_cast<const uint16_t*>(xb + (ks >> 1) * 2048 + (ks & 1) * 1024);
+      const bf16x8 pt = concat4(lds_tr8(rb, pr_b0), lds_tr8(rb, (pr_b0 ^ 16) + 256));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pt, kq[ks], acc, 0, 0, 0);
+    }
+    // element i of lane (n, g): row position (i/4)*8 + g*4 + i%4, dim 32 wave + n
+    float* dst = dq_acc + s * rs + (int64_t)h * kD + wave * 32 + n;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = (i >> 2) * 8 + g * 4 + (i & 3);
+      const int row = r0h + (2 * (m >> 4) + ((m & 7) >> 2)) * 8 + ((m >> 3) & 1) * 4 + (m & 3);
+      if (row < L) unsafeAtomicAdd(dst + (int64_t)row * rs, acc[i]);
+    }
+  };
+
   // one 64-row step (two halves of 32 rows) from LDS stage `stage`; `next`
   // (>= 0) is the next step's first row, whose DMA is issued after this
   // step's func loads
@@ -307,6 +371,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_kv(
         }
       }
       if constexpr (kStoreP) p_store(q0 + hf * kKvBM, pb);
+      if constexpr (kAtomicDQ) dq_atomic(q0 + hf * kKvBM, hf, pb);
       // dV^T += dO^T Y and dK^T += Q^T P: A operands by transpose reads, query
       // rows 16hh + 4g + {0..3} and 16hh + 8 + 4g + {0..3}; the operands of
       // step o + 1 (o = 4 hh + mb) are read before the products of step o so
@@ -592,12 +657,12 @@ hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const vo
   const float scale = alpha * inv_max_len;
   if (Ukv.cap > 0) {
     ProfScope ps(stream, pstore ? "k_bwd_kv_p" : "k_bwd_kv");
-    auto kern = pstore ? k_bwd_kv<true> : k_bwd_kv<false>;
+    auto kern = pstore ? k_bwd_kv<true, false> : k_bwd_kv<false, false>;
     hipLaunchKernelGGL(kern, dim3(Ukv.cap), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout),
                        static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), P, Ukv.list, H,
-                       func, nfunc, alpha, scale, pstore, pstore_cap);
+                       func, nfunc, alpha, scale, pstore, pstore_cap, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -608,6 +673,68 @@ hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const vo
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout),
                        static_cast<uint16_t*>(dq), P, Uq.list, H, func, nfunc, alpha, scale);
+  }
+  return hipGetLastError();
+}
+
+namespace {
+
+// fp32 accumulator of the atomic-dQ backward: cleared by a kernel (not a
+// memset, so that the enqueued work can be captured in a graph) and turned
+// into bf16 dq = acc * scale afterwards.  n4 = elements / 4 (D = 128, so a
+// whole number).
+__global__ __launch_bounds__(256) void k_fill_f32(float4* __restrict__ p, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__global__ __launch_bounds__(256) void k_dq_convert(const float4* __restrict__ acc,
+                                                    uint16_t* __restrict__ dq, int64_t n4,
+                                                    float scale) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * 256) {
+    const float4 a = acc[i];
+    bf16x4 w;
+    w[0] = (__bf16)(a.x * scale);
+    w[1] = (__bf16)(a.y * scale);
+    w[2] = (__bf16)(a.z * scale);
+    w[3] = (__bf16)(a.w * scale);
+    *reinterpret_cast<bf16x4*>(dq + 4 * i) = w;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mfma_bwd_atomic(const void* q, const void* k, const void* v, const void* dout,
+                                  void* dq, void* dk, void* dv, const Prep& P, const Units& Ukv,
+                                  int H, const int32_t* func, int nfunc, float alpha,
+                                  float inv_max_len, float* dq_acc, int64_t total,
+                                  hipStream_t stream) {
+  const float scale = alpha * inv_max_len;
+  const int64_t n4 = total * H * kD / 4;
+  const int grid = (int)std::min<int64_t>(std::max<int64_t>((n4 + 255) / 256, 1), 8192);
+  if (n4 > 0) {
+    ProfScope ps(stream, "k_fill_f32");
+    hipLaunchKernelGGL(k_fill_f32, dim3(grid), dim3(256), 0, stream,
+                       reinterpret_cast<float4*>(dq_acc), n4);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (Ukv.cap > 0) {
+    ProfScope ps(stream, "k_bwd_kv_atomic");
+    hipLaunchKernelGGL((k_bwd_kv<false, true>), dim3(Ukv.cap), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dout),
+                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), P, Ukv.list, H,
+                       func, nfunc, alpha, scale, nullptr, (uint64_t)0, dq_acc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (n4 > 0) {
+    ProfScope ps(stream, "k_dq_convert");
+    hipLaunchKernelGGL(k_dq_convert, dim3(grid), dim3(256), 0, stream,
+                       reinterpret_cast<const float4*>(dq_acc), static_cast<uint16_t*>(dq), n4,
+                       scale);
   }
   return hipGetLastError();
 }

@@ -159,6 +159,11 @@ hipError_t launch_mfma_bwd(const void* q, const void* k, const void* v, const vo
                            const Units& Uq, int H, const int32_t* func, int nfunc, float alpha,
                            float inv_max_len, uint16_t* pstore, uint64_t pstore_cap,
                            hipStream_t stream);
+hipError_t launch_mfma_bwd_atomic(const void* q, const void* k, const void* v, const void* dout,
+                                  void* dq, void* dk, void* dv, const Prep& P, const Units& Ukv,
+                                  int H, const int32_t* func, int nfunc, float alpha,
+                                  float inv_max_len, float* dq_acc, int64_t total,
+                                  hipStream_t stream);
 hipError_t launch_dq_from_p(const void* k, void* dq, const Prep& P, const Units& Uq, int H,
                             int nfunc, const uint16_t* pstore, uint64_t pstore_cap,
                             float out_scale, hipStream_t stream);

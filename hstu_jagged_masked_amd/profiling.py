@@ -33,9 +33,10 @@ import re
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNELS = ("k_fwd_bf16", "k_bwd_kv", "k_bwd_kv_p", "k_bwd_q", "k_bwd_dq", "k_targets_fwd",
-           "k_targets_bwd")
+KERNELS = ("k_fwd_bf16", "k_bwd_kv", "k_bwd_kv_p", "k_bwd_kv_atomic", "k_bwd_q", "k_bwd_dq",
+           "k_targets_fwd", "k_targets_bwd")
 KERNEL_SOURCES = {"k_fwd_bf16": ["fwd.hip"], "k_bwd_kv": ["bwd.hip"], "k_bwd_kv_p": ["bwd.hip"],
+                  "k_bwd_kv_atomic": ["bwd.hip"],
                   "k_bwd_q": ["bwd.hip"],
                   "k_bwd_dq": ["dq.hip"], "k_targets_fwd": ["targets.hip"],
                   "k_targets_bwd": ["targets.hip"]}
@@ -52,10 +53,17 @@ def source_digest(kernel: str) -> str:
 
 
 def short_name(name: str) -> str:
-    m = re.search(r"(k_\w+)(<true>)?", name)
+    m = re.search(r"(k_\w+)(<[^>]*>)?", name)
     if m and "hstu" in name:
-        # the key-owner kernel's stored-P instantiation is named as in the library's own timing
-        return m.group(1) + ("_p" if m.group(1) == "k_bwd_kv" and m.group(2) else "")
+        # the key-owner kernel's instantiations <store P, atomic dQ> are named
+        # as in the library's own timing
+        if m.group(1) == "k_bwd_kv" and m.group(2):
+            targs = [a.strip() for a in m.group(2)[1:-1].split(",")]
+            if targs[0] == "true":
+                return "k_bwd_kv_p"
+            if len(targs) > 1 and targs[1] == "true":
+                return "k_bwd_kv_atomic"
+        return m.group(1)
     return name.split("(")[0][-60:]
 
 
@@ -213,8 +221,10 @@ def isa_blocks(asm_text: str):
 def short_name_isa(symbol: str) -> str:
     m = re.search(r"(k_\w+?)(I[LbB0-9E]+)?E", symbol)
     name = m.group(1) if m else symbol[:40]
-    if name == "k_bwd_kv" and "ILb1E" in symbol:
+    if name == "k_bwd_kv" and "k_bwd_kvILb1E" in symbol:
         name = "k_bwd_kv_p"
+    elif name == "k_bwd_kv" and "k_bwd_kvILb0ELb1E" in symbol:
+        name = "k_bwd_kv_atomic"
     return name
 
 
@@ -224,7 +234,7 @@ def isa(build_dir: str = None) -> str:
     build_dir = build_dir or bld.BUILD
     os.makedirs(build_dir, exist_ok=True)
     flags = [f for f in bld.COMPILE_FLAGS if not f.startswith("-Rpass")]
-    lines = ["kernel        block       mfma trans valu  lds_rd | per 64 elements: valu trans "
+    lines = ["kernel           block       mfma trans valu  lds_rd | per 64 elements: valu trans "
              "(valu = other vector ALU instructions)"]
     for src in ISA_SOURCES:
         out = os.path.join(build_dir, src + ".s")
@@ -243,7 +253,7 @@ def isa(build_dir: str = None) -> str:
                            not k.startswith(("v_mfma", "v_accvgpr") + TRANSCENDENTAL))
                 lds = sum(v for k, v in ops.items() if k.startswith("ds_read"))
                 per = (f"{valu / (trans / 2):6.2f} {2.0:5.1f}" if trans else "")
-                lines.append(f"{kernel:13s} {block:11s} {mfma:4d} {trans:5d} {valu:4d} {lds:6d}"
+                lines.append(f"{kernel:16s} {block:11s} {mfma:4d} {trans:5d} {valu:4d} {lds:6d}"
                              f" | {per}")
     return "\n".join(lines)
 

@@ -180,6 +180,26 @@ int hstu_attn_bwd_pstore_chunked(const void* q, const void* k, const void* v, co
                                  int64_t max_len, void* workspace, size_t workspace_bytes,
                                  void* pstore, size_t pstore_bytes, void* stream);
 
+/* Atomic-dQ backward (bf16, D = 128, full-length mode): the same dk and dv as
+ * hstu_attn_bwd, bitwise, and dq up to the order of fp32 additions.  It is the
+ * variant the pages rank against the deterministic dQ kernel (MLCommons
+ * training PR #903, "Read First": gradients close rather than bitwise equal
+ * are acceptable): the key-owner pass also forms, for every 32-row half it
+ * walks, the dQ contribution of its 128 keys and adds it to dq_accum with
+ * fp32 atomics, so there is neither a query-owner pass that recomputes
+ * <q_i, k_j> and <dO_i, v_j> nor a stored P.  The additions reach each
+ * element in no fixed order: dq is not bitwise repeatable.
+ * dq_accum: device buffer of at least total*H*D*4 bytes (fp32 [total, H, D]),
+ * 256-byte aligned; scratch (cleared and overwritten by the call).  dq is
+ * written from it (times alpha/max_len, rounded to bf16) after the pass.
+ * Workspace and other arguments as hstu_attn_bwd; the call enqueues its work
+ * and returns without synchronizing `stream`. */
+int hstu_attn_bwd_atomic(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                         void* dk, void* dv, const int64_t* seq_offsets, int64_t B, int64_t total,
+                         int H, int D, const int32_t* func, int nfunc, float alpha,
+                         int64_t max_len, void* workspace, size_t workspace_bytes, void* dq_accum,
+                         size_t dq_accum_bytes, void* stream);
+
 /* Visible-column count |V_i| of every query row: counts is int32 [total]
  * (or [B] with target_rows), total_pairs a device int64 receiving their sum.
  * Either output may be NULL.  Integer work: exact. */

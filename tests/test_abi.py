@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     assert names == sorted(["hstu_max_nfunc", "hstu_last_error", "hstu_attn_workspace_size",
                             "hstu_attn_fwd", "hstu_attn_fwd_noalloc", "hstu_attn_bwd",
                             "hstu_attn_bwd_pstore", "hstu_attn_bwd_pstore_chunked",
-                            "hstu_attn_pstore_bytes", "hstu_attn_visible_counts",
+                            "hstu_attn_bwd_atomic", "hstu_attn_pstore_bytes", "hstu_attn_visible_counts",
                             "hstu_attn_check_inputs", "hstu_profile_enable",
                             "hstu_profile_read", "hstu_profile_reset"])
 
@@ -197,6 +197,30 @@ def test_bwd_pstore_chunked_rejects_bad_arguments(lib):
     # lengths 100, 200 at H = 2: 4 and 14 blocks of 8 KiB per head
     st, msg = call([0, 100, 300], 14 * 2 * 8192 - 1)
     assert st == -1 and "sequence 1 needs 229376 bytes" in msg
+
+
+def test_bwd_atomic_rejects_bad_arguments(lib):
+    """The atomic-dQ backward refuses D != 128 and a missing, misaligned or
+    too small fp32 accumulator on the host, before anything is enqueued (the
+    library never touches the fake device pointers)."""
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    total, H = 300, 2
+    need = total * H * 128 * 4
+
+    def call(acc, acc_bytes, D=128):
+        st = lib.hstu_attn_bwd_atomic(f, f, f, f, f, f, f, f, 2, total, H, D, f, 5, 0.1, 8, f,
+                                      1 << 20, acc, acc_bytes, None)
+        return st, lib.hstu_last_error().decode()
+
+    st, msg = call(f, need, D=64)
+    assert st == -2 and "needs D = 128" in msg
+    st, msg = call(None, need)
+    assert st == -1 and "dq_accum is NULL" in msg
+    st, msg = call(P(FAKE + 16), need)
+    assert st == -1 and "256-byte aligned" in msg
+    st, msg = call(f, need - 4)
+    assert st == -1 and f"needs {need}" in msg
 
 
 def test_fwd_noalloc_rejects_sizes_beyond_its_array(lib):

@@ -284,6 +284,42 @@ def test_stored_p_bitwise_repeatable(hj):
             assert torch.equal(a, b)
 
 
+ATOMIC_CASES = {
+    "causal_ragged": ([700, 1, 300, 0, 1000, 64, 129], 3, lambda ls: wl.func_causal(ls, 5)),
+    "long_windows": ([4700, 300], 1, lambda ls: wl.func_causal(ls, 5)),
+    "sla": ([1024, 777, 2048], 2, lambda ls: wl.func_sla(ls, 256, 32, 5)),
+    "random_nfunc9": ([500, 333, 64], 2, lambda ls: wl.func_random(ls, 9, 91, spread=20)),
+    "three_interval": ([900, 611], 2, lambda ls: wl.func_three_interval(ls, 16, 8, 5)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ATOMIC_CASES))
+def test_bf16_atomic_dq(hj, case):
+    """The atomic-dQ backward (dQ added with fp32 atomics by the key-owner
+    pass): dq within the bf16 bound of the oracle and close to attn_bwd's, dk
+    and dv bitwise those of attn_bwd (the same key-owner arithmetic), and the
+    accumulator's previous contents (NaN here) never reach dq."""
+    lengths, H, make_func = ATOMIC_CASES[case]
+    ls = np.asarray(lengths, dtype=np.int64)
+    f = make_func(ls)
+    off = wl.offsets_from_lengths(ls)
+    inp = make_inputs(ls, H, 128, "bf16", 31)
+    (q, qn), (k, kn), (v, vn), (do, don) = inp["q"], inp["k"], inp["v"], inp["do"]
+    off_t = torch.from_numpy(off).to(DEV)
+    ft = torch.from_numpy(np.ascontiguousarray(f)).to(DEV)
+    alpha, max_len = 0.11, int(ls.max()) + 1
+    args = (q, k, v, do, off_t, ft, alpha, max_len)
+    acc = torch.full((int(off[-1]), H, 128), float("nan"), dtype=torch.float32, device=DEV)
+    dq, dk, dv = hj.attn_bwd_atomic(*args, dq_accum=acc)
+    rq, rk, rv = hj.attn_bwd(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, rk) and torch.equal(dv, rv)
+    wq, _, _ = oracle.bwd(qn, kn, vn, don, off, f, alpha, max_len, None)
+    assert_parity("dq", dq, wq, "bf16")
+    scale = max(1.0, float(rq.float().abs().max().item()))
+    assert float((dq.float() - rq.float()).abs().max().item()) <= 2e-2 * scale
+
+
 @pytest.mark.parametrize("targets", [False, True])
 def test_autograd_wrapper_matches_entry_points(hj, targets):
     """hstu_attention (torch.autograd.Function): the forward and the gradients
