@@ -66,7 +66,7 @@ def to64(x):
     return x.float().cpu().numpy().astype(np.float64)
 
 
-def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False, pstore=False):
+def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False, pstore=False, atomic=False):
     """fwd+bwd on the whole workload; oracle on the sequences `seqs`.  With
     `repeat`, a second fwd+bwd must reproduce every output bit for bit (each
     output element is written by one workgroup in a fixed order, so any
@@ -74,7 +74,9 @@ def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False, pstore=False)
     the default one, on the same inputs) and is checked against the same
     oracle values, and its dk, dv must equal the default path's bit for bit;
     run over a buffer of about a seventh of the batch's stored P, in runs of
-    sequences, it must reproduce its own outputs bit for bit."""
+    sequences, it must reproduce its own outputs bit for bit.  With `atomic`,
+    the atomic-dQ backward runs too: dk, dv bitwise the default path's, dq
+    against the oracle."""
     t, off = device_inputs(cfg)
     func = torch.from_numpy(func_np).to(DEV)
     o = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], func, cfg["alpha"], cfg["max_len"])
@@ -113,6 +115,11 @@ def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False, pstore=False)
             assert torch.equal(a, b), f"{cfg['name']}.pstore chunked ({budget} B).{nm} differs"
         del ps, gc
         assert torch.equal(gp[1], dk) and torch.equal(gp[2], dv), "stored-P dk/dv differ"
+    ga = None
+    if atomic:
+        ga = hj.attn_bwd_atomic(t["q"], t["k"], t["v"], t["do"], t["off"], func, cfg["alpha"],
+                                cfg["max_len"])
+        assert torch.equal(ga[1], dk) and torch.equal(ga[2], dv), "atomic-dQ dk/dv differ"
     torch.cuda.synchronize()
     rows, sub_off = oracle.subset(off, seqs)
     rows_t = torch.from_numpy(rows).to(DEV)
@@ -125,6 +132,8 @@ def run_full(hj, cfg, func_np, seqs, nfunc_label="", repeat=False, pstore=False)
         check(f"{cfg['name']}{nfunc_label}.{nm}", got.index_select(0, rows_t), w)
     if gp is not None:
         check(f"{cfg['name']}{nfunc_label}.pstore.dq", gp[0].index_select(0, rows_t), want[0])
+    if ga is not None:
+        check(f"{cfg['name']}{nfunc_label}.atomic.dq", ga[0].index_select(0, rows_t), want[0])
     return (o, dq, dk, dv), t, off
 
 
@@ -156,7 +165,7 @@ def test_sla_1k_full(hj):
 def test_sla_2k_full_and_nfunc3_bitwise(hj):
     cfg = wl.workload("sla_2k")
     ls = cfg["lengths"]
-    out5, t, off = run_full(hj, cfg, cfg["func"](ls, 5), list(range(len(ls))))
+    out5, t, off = run_full(hj, cfg, cfg["func"](ls, 5), list(range(len(ls))), atomic=True)
     f3 = torch.from_numpy(cfg["func"](ls, 3)).to(DEV)
     o3 = hj.attn_fwd(t["q"], t["k"], t["v"], t["off"], f3, cfg["alpha"], cfg["max_len"])
     g3 = hj.attn_bwd(t["q"], t["k"], t["v"], t["do"], t["off"], f3, cfg["alpha"], cfg["max_len"])
@@ -174,7 +183,7 @@ def test_hstu_layer_shapes_sampled(hj, name):
     cfg = wl.workload(name)
     ls = cfg["lengths"]
     f = cfg["func"](ls, 5)
-    run_full(hj, cfg, f, sample_seqs(ls), repeat=True, pstore=True)
+    run_full(hj, cfg, f, sample_seqs(ls), repeat=True, pstore=True, atomic=name == "hstu_2663")
     off_t = torch.from_numpy(wl.offsets_from_lengths(ls)).to(DEV)
     counts, tot = hj.visible_counts(off_t, torch.from_numpy(f).to(DEV), int(ls.sum()))
     assert np.array_equal(counts.cpu().numpy(), wl.local_rows(ls) + 1), "causal counts"

@@ -418,6 +418,25 @@ def test_random_sweep(hj, seed):
 
 
 @pytest.mark.parametrize("seed", range(max(4, SWEEP_CASES // 2)))
+def test_random_sweep_atomic(hj, seed):
+    """The atomic-dQ backward on the sweep's full-length configurations: dq
+    against the oracle, dk and dv bitwise those of attn_bwd."""
+    ls, H, f, alpha, max_len, path, _ = random_case(seed)
+    print(f"seed {seed}: lengths {ls.tolist()} H {H} nfunc {f.shape[0]}", flush=True)
+    off = wl.offsets_from_lengths(ls)
+    off_t = torch.from_numpy(off).to(DEV)
+    inp = make_inputs(ls, H, 128, "bf16", 5000 + seed)
+    (q, qn), (k, kn), (v, vn), (do, don) = inp["q"], inp["k"], inp["v"], inp["do"]
+    args = (q, k, v, do, off_t, torch.from_numpy(np.ascontiguousarray(f)).to(DEV), alpha, max_len)
+    dq, dk, dv = hj.attn_bwd_atomic(*args)
+    _, rk, rv = hj.attn_bwd(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, rk) and torch.equal(dv, rv)
+    wq, _, _ = oracle.bwd(qn, kn, vn, don, off, f, alpha, max_len, None)
+    assert_parity("dq", dq, wq, "bf16")
+
+
+@pytest.mark.parametrize("seed", range(max(4, SWEEP_CASES // 2)))
 def test_random_sweep_generic(hj, seed):
     """The plain-FMA kernels (fp32 at D = 32, 64, 128; bf16 at D = 32, 64) on
     random configurations against the oracle, full-length and targets-only."""
