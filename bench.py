@@ -13,6 +13,8 @@ counting 4*D (forward) + 10*D (backward) flops per visible (query, key) pair and
 head, over unmasked pairs only.  Also reported: per-step median and minimum
 over 3 further runs and the spread of their medians (step_stats), the
 targets-only mode (one candidate row per sequence against full-length K/V),
+the backward alone with each dQ path (stored P, recompute, fp32 atomics:
+dq_variants),
 per-kernel times measured with HIP events on the launch stream during the
 timed steps, the roofline of the dominant kernel, the other workloads at their
 full sizes (per_workload: SLA 1k / 2k, three-interval, OneRank, ragged, L=4086,
