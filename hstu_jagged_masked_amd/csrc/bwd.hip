@@ -39,6 +39,7 @@
 // atomics (in no fixed order: dq is not bitwise repeatable).
 #include <type_traits>
 
+#include "atomic_dq.h"
 #include "common.h"
 #include "pstore.h"
 #include "tiles.h"
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kThreads, kAtomicDQ ? 1 : 2) void k_bwd_kv(
   __shared__ int sPart[kStepWin], sFull[kStepWin];
   __shared__ int sCount[2];
   // atomic dQ: per half, the four waves' P registers (2 KiB each)
-  __shared__ __attribute__((aligned(16))) uint16_t sX[kAtomicDQ ? 2 * 4 * 1024 : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[kAtomicDQ ? kXchgBytes / 2 : 8];
 
   UnitRec u;
   if (!unit_of_block(units, u)) return;
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(kThreads, kAtomicDQ ? 1 : 2) void k_bwd_kv(
     for (int ks = 0; ks < kKvBN / 16; ++ks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int key = c0 + 16 * ks + 8 * g + e;
+        const int key = c0 + xchg_k_key(ks, g, e);
         const uint16_t bits = key < L ? kd[(int64_t)key * rs] : (uint16_t)0;
         kq[ks][e] = __builtin_bit_cast(__bf16, bits);
       }
@@ -261,37 +262,30 @@ __global__ __launch_bounds__(kThreads, kAtomicDQ ? 1 : 2) void k_bwd_kv(
   const int tr_b0 = trow * 256 + 8 * (gl & 1) +
                     ((((grp & 1) * 2 + ((gl & 3) >> 1)) ^ swz(trow)) << 4);
 
-  // Atomic dQ of one half (query rows from r0h): each wave writes its P
-  // registers to the half's exchange buffer (2 KiB per wave: key rows of 64
-  // bytes, the 16-byte chunk of lane (n, g) at g ^ ((n/4) mod 4)), and reads
-  // the tile's 128 keys back with transpose reads, so that lane l holds keys
-  // 16 ks + 8 (l/32) + 0..7 of row position l % 32: the A operand of
-  // dQ[row position][dim] += P K.  Row position hh*16 + g'*8 + e is query row
-  // (2 hh + e/4)*8 + g'*4 + e%4 of the half (the order of the P registers).
-  // The two halves use separate buffers; the barrier before each step
-  // retires a buffer before the next step rewrites it.
-  const int pw_b0 = n * 64 + ((g ^ ((n >> 2) & 3)) << 4);
-  const int pr_b0 = (8 * (grp >> 1) + (gl >> 2)) * 64 +
-                    ((((grp & 1) * 2 + ((gl & 3) >> 1)) ^ (2 * (grp >> 1))) << 4) +
-                    (gl & 1) * 8;
+  // Atomic dQ of one half (query rows from r0h), in the exchange layout of
+  // atomic_dq.h.  The two halves use separate buffers; the barrier before
+  // each step retires a buffer before the next step rewrites it.
   auto dq_atomic = [&](int r0h, int hf, const bf16x8* pv) {
-    char* xb = reinterpret_cast<char*>(sX) + hf * 8192;
-    *reinterpret_cast<bf16x8*>(xb + wave * 2048 + pw_b0) = pv[0];
-    *reinterpret_cast<bf16x8*>(xb + wave * 2048 + (pw_b0 ^ 32)) = pv[1];
+    const int xw0 = xchg_write_offset(wave, n, g, 0), xw1 = xchg_write_offset(wave, n, g, 1);
+    const int xr0 = xchg_read_offset(lane, 0, 0), xr1 = xchg_read_offset(lane, 0, 1);
+    char* xb = reinterpret_cast<char*>(sX) + hf * kXchgHalfBytes;
+    *reinterpret_cast<bf16x8*>(xb + xw0) = pv[0];
+    *reinterpret_cast<bf16x8*>(xb + xw1) = pv[1];
     lds_barrier();
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kKvBN / 16; ++ks) {
-      const uint16_t* rb = reinterpret_cast<const uint16_t*>(xb + (ks >> 1) * 2048 + (ks & 1) * 1024);
-      const bf16x8 pt = concat4(lds_tr8(rb, pr_b0), lds_tr8(rb, (pr_b0 ^ 16) + 256));
+      // xchg_read_offset(lane, ks, s) = xchg_read_offset(lane, 0, s) + this
+      const uint16_t* rb = reinterpret_cast<const uint16_t*>(
+          xb + (ks >> 1) * kXchgWaveBytes + (ks & 1) * 1024);
+      const bf16x8 pt = concat4(lds_tr8(rb, xr0), lds_tr8(rb, xr1));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pt, kq[ks], acc, 0, 0, 0);
     }
-    // element i of lane (n, g): row position (i/4)*8 + g*4 + i%4, dim 32 wave + n
+    // element i of lane (n, g): dim 32 wave + n of query row r0h + xchg_acc_row(i, g)
     float* dst = dq_acc + s * rs + (int64_t)h * kD + wave * 32 + n;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int m = (i >> 2) * 8 + g * 4 + (i & 3);
-      const int row = r0h + (2 * (m >> 4) + ((m & 7) >> 2)) * 8 + ((m >> 3) & 1) * 4 + (m & 3);
+      const int row = r0h + xchg_acc_row(i, g);
       if (row < L) unsafeAtomicAdd(dst + (int64_t)row * rs, acc[i]);
     }
   };

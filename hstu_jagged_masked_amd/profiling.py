@@ -36,7 +36,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 KERNELS = ("k_fwd_bf16", "k_bwd_kv", "k_bwd_kv_p", "k_bwd_kv_atomic", "k_bwd_q", "k_bwd_dq",
            "k_targets_fwd", "k_targets_bwd")
 KERNEL_SOURCES = {"k_fwd_bf16": ["fwd.hip"], "k_bwd_kv": ["bwd.hip"], "k_bwd_kv_p": ["bwd.hip"],
-                  "k_bwd_kv_atomic": ["bwd.hip"],
+                  "k_bwd_kv_atomic": ["bwd.hip", "atomic_dq.h"],
                   "k_bwd_q": ["bwd.hip"],
                   "k_bwd_dq": ["dq.hip"], "k_targets_fwd": ["targets.hip"],
                   "k_targets_bwd": ["targets.hip"]}
