@@ -50,3 +50,18 @@ def test_key_owner_step_is_the_silu_prime_count(per_element):
 
 def test_every_mfma_kernel_has_silu_blocks(per_element):
     assert {"k_fwd_bf16", "k_bwd_kv", "k_bwd_kv_p", "k_bwd_q"} <= set(per_element)
+
+
+def test_profile_names_of_the_key_owner_instantiations():
+    """rocprofv3 and the assembly name the key-owner kernel's instantiations
+    by their template arguments <store P, atomic dQ>; the summaries and the
+    HBM-traffic table use the library's own timing names."""
+    base = "void hstu::(anonymous namespace)::k_bwd_kv<{}>(unsigned short const*, int)"
+    assert profiling.short_name(base.format("true, false")) == "k_bwd_kv_p"
+    assert profiling.short_name(base.format("false, false")) == "k_bwd_kv"
+    assert profiling.short_name(base.format("false, true")) == "k_bwd_kv_atomic"
+    assert profiling.short_name("hstu::(anonymous namespace)::k_fwd_bf16(int)") == "k_fwd_bf16"
+    mangled = "_ZN4hstu12_GLOBAL__N_18k_bwd_kvILb{}ELb{}EEEvPKtS3_"
+    assert profiling.short_name_isa(mangled.format(1, 0)) == "k_bwd_kv_p"
+    assert profiling.short_name_isa(mangled.format(0, 0)) == "k_bwd_kv"
+    assert profiling.short_name_isa(mangled.format(0, 1)) == "k_bwd_kv_atomic"
